@@ -1,0 +1,158 @@
+"""ctypes binding of libsparse_attn.so: argument marshalling only.
+
+Every function has the name and argument order of the C entry point in
+include/sparse_attn.h; tensors are passed by device pointer (``data_ptr``)
+and the stream is torch's current HIP stream unless one is given.  Nothing
+here computes any part of the path.  A missing library raises immediately:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libsparse_attn.so")
+
+SA_OK = 0
+SA_ERR_INVALID_ARG = -1
+SA_ERR_UNSUPPORTED = -2
+SA_ERR_WORKSPACE = -3
+SA_ERR_HIP = -4
+SA_ERR_CAPACITY = -5
+
+SA_F32, SA_BF16 = 0, 1
+SA_TOP_P, SA_TOP_K = 0, 1
+SA_SCORE_POOLED, SA_SCORE_LOWRANK = 0, 1
+SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD = 0, 1, 2, 3
+
+EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
+           "kv_demand_pack", "sparse_attn_forward", "sa_status_string", "sa_abi_version")
+
+
+class SaProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("q_rows", ctypes.c_int64),
+        ("q_valid", ctypes.c_int64),
+        ("kv_rows", ctypes.c_int64),
+        ("kv_valid", ctypes.c_int64),
+        ("sm_scale", ctypes.c_float),
+        ("score_scale", ctypes.c_float),
+        ("select_mode", ctypes.c_int32),
+        ("top_p", ctypes.c_float),
+        ("top_k", ctypes.c_int32),
+        ("score_mode", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+    ]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {status} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_attention_scores_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    prob = ctypes.POINTER(SaProblem)
+    lib.sa_workspace_size.argtypes = [prob, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.sparse_attn_select.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.sparse_attn_csr_from_mask.argtypes = [prob, P, P, P, P, sz, P]
+    lib.kv_demand_pack.argtypes = [prob, P, P, P, P, P, P, P, P, P, i64, P, P, sz, P]
+    lib.sparse_attn_forward.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.sa_status_string.argtypes = [ctypes.c_int]
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_abi_version.argtypes = []
+    for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
+                 "kv_demand_pack", "sparse_attn_forward", "sa_abi_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().sa_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != SA_OK:
+        raise SparseAttnError(fn, status, status_string(status))
+
+
+def problem(heads, head_dim, block, dtype, q_rows, q_valid, kv_rows, kv_valid,
+            sm_scale=0.0, score_scale=0.0, select_mode=SA_TOP_P, top_p=0.9, top_k=1,
+            score_mode=SA_SCORE_POOLED, rank=16) -> SaProblem:
+    return SaProblem(heads, head_dim, block, dtype, q_rows, q_valid, kv_rows, kv_valid,
+                     sm_scale, score_scale, select_mode, top_p, top_k, score_mode, rank)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- entry points, same names and argument order as the C ABI --------------
+def sa_workspace_size(prob: SaProblem, stage: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sa_workspace_size", load().sa_workspace_size(ctypes.byref(prob), stage, ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_select(prob, q, k, wq, wk, mask_bits, row_ptr, col_idx, qbar_opt, kbar_opt,
+                       ws, ws_bytes, stream=None):
+    _check("sparse_attn_select", load().sparse_attn_select(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(mask_bits), _ptr(row_ptr),
+        _ptr(col_idx), _ptr(qbar_opt), _ptr(kbar_opt), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_csr_from_mask(prob, mask_bits, row_ptr, col_idx, ws, ws_bytes, stream=None):
+    _check("sparse_attn_csr_from_mask", load().sparse_attn_csr_from_mask(
+        ctypes.byref(prob), _ptr(mask_bits), _ptr(row_ptr), _ptr(col_idx), _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def kv_demand_pack(prob, row_ptr, col_idx, k, v, demand_ptr, demand_idx, col_slot, k_packed,
+                   v_packed, packed_cap_blocks, dev_status, ws, ws_bytes, stream=None):
+    _check("kv_demand_pack", load().kv_demand_pack(
+        ctypes.byref(prob), _ptr(row_ptr), _ptr(col_idx), _ptr(k), _ptr(v), _ptr(demand_ptr),
+        _ptr(demand_idx), _ptr(col_slot), _ptr(k_packed), _ptr(v_packed), int(packed_cap_blocks),
+        _ptr(dev_status), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_forward(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
+                        ws_bytes, stream=None):
+    _check("sparse_attn_forward", load().sparse_attn_forward(
+        ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
+        _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

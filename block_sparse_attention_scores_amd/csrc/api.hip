@@ -1,0 +1,247 @@
+// C ABI of the block-sparse attention path: argument validation (before any
+// HIP call), workspace carving and the launch sequence of every entry point.
+// The operations themselves are documented in include/sparse_attn.h.
+#include <math.h>
+#include <string.h>
+
+#include "sa_common.h"
+
+namespace sa {
+bool attn_supported(int dtype, int d, int B);
+}
+
+namespace {
+
+using sa::Dims;
+
+constexpr int kMaxKB = 4096;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the problem and fills the derived sizes.  No HIP call.
+int check_problem(const sa_problem* p, Dims* g) {
+  if (!p) return SA_ERR_INVALID_ARG;
+  if (p->num_heads < 1) return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  if (p->head_dim < 1 || p->block < 1) return SA_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (p->block != 64 && p->block != 128) return SA_ERR_UNSUPPORTED;
+  const int64_t B = p->block;
+  if (p->q_rows < B || p->q_rows % B || p->kv_rows < B || p->kv_rows % B) return SA_ERR_INVALID_ARG;
+  if (p->q_valid <= p->q_rows - B || p->q_valid > p->q_rows) return SA_ERR_INVALID_ARG;
+  if (p->kv_valid <= p->kv_rows - B || p->kv_valid > p->kv_rows) return SA_ERR_INVALID_ARG;
+  const int64_t nqb = p->q_rows / B, nkb = p->kv_rows / B;
+  if (nkb > kMaxKB) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_heads * nqb * nkb >= ((int64_t)1 << 31)) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_heads * p->kv_rows * p->head_dim >= ((int64_t)1 << 40)) return SA_ERR_UNSUPPORTED;
+  if (p->select_mode != SA_TOP_P && p->select_mode != SA_TOP_K) return SA_ERR_INVALID_ARG;
+  if (p->select_mode == SA_TOP_P && !(p->top_p > 0.f)) return SA_ERR_INVALID_ARG;
+  if (p->select_mode == SA_TOP_P && p->top_k < 0) return SA_ERR_INVALID_ARG;
+  if (p->select_mode == SA_TOP_K && p->top_k < 1) return SA_ERR_INVALID_ARG;
+  if (p->score_mode != SA_SCORE_POOLED && p->score_mode != SA_SCORE_LOWRANK) return SA_ERR_INVALID_ARG;
+  if (p->score_mode == SA_SCORE_LOWRANK && (p->rank < 1 || p->rank > 64)) return SA_ERR_INVALID_ARG;
+  if (!isfinite(p->sm_scale) || !isfinite(p->score_scale)) return SA_ERR_INVALID_ARG;
+  g->H = p->num_heads;
+  g->d = p->head_dim;
+  g->B = p->block;
+  g->nqb = (int)nqb;
+  g->nkb = (int)nkb;
+  g->W = (int)((nkb + 31) / 32);
+  g->rank = p->score_mode == SA_SCORE_LOWRANK ? p->rank : 0;
+  g->q_rows = p->q_rows;
+  g->q_valid = p->q_valid;
+  g->kv_rows = p->kv_rows;
+  g->kv_valid = p->kv_valid;
+  g->dtype = p->dtype;
+  return SA_OK;
+}
+
+// Workspace layout of every stage, in carve order.
+struct SelectWs {
+  size_t qbar, kbar, qt, kt, scores, counts, total;
+};
+SelectWs select_ws(const Dims& g) {
+  SelectWs w{};
+  size_t o = 0;
+  w.qbar = o; o += round_up(sizeof(double) * g.H * g.nqb * g.d);
+  w.kbar = o; o += round_up(sizeof(double) * g.H * g.nkb * g.d);
+  w.qt = o; o += round_up(sizeof(double) * g.H * g.nqb * g.rank);
+  w.kt = o; o += round_up(sizeof(double) * g.H * g.nkb * g.rank);
+  w.scores = o; o += round_up(sizeof(double) * g.H * g.nqb * g.nkb);
+  w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nqb);
+  w.total = o;
+  return w;
+}
+size_t csr_ws(const Dims& g) { return round_up(sizeof(int32_t) * g.H * g.nqb); }
+struct PackWs {
+  size_t bits, heads, total;
+};
+PackWs pack_ws(const Dims& g) {
+  PackWs w{};
+  size_t o = 0;
+  w.bits = o; o += round_up(sizeof(uint32_t) * g.H * g.W);
+  w.heads = o; o += round_up(sizeof(int32_t) * g.H);
+  w.total = o;
+  return w;
+}
+size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * g.H * g.nqb); }
+
+size_t stage_bytes(const Dims& g, int stage) {
+  switch (stage) {
+    case SA_STAGE_SELECT: return select_ws(g).total;
+    case SA_STAGE_CSR: return csr_ws(g);
+    case SA_STAGE_PACK: return pack_ws(g).total;
+    case SA_STAGE_FORWARD: return forward_ws(g);
+  }
+  return 0;
+}
+
+int check_ws(const Dims& g, int stage, void* ws, size_t ws_bytes) {
+  const size_t need = stage_bytes(g, stage);
+  if (need == 0) return SA_OK;
+  if (!ws || ((uintptr_t)ws % kAlign)) return SA_ERR_INVALID_ARG;
+  if (ws_bytes < need) return SA_ERR_WORKSPACE;
+  return SA_OK;
+}
+
+#define SA_TRY_HIP(expr)                          \
+  do {                                            \
+    if ((expr) != hipSuccess) return SA_ERR_HIP;  \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_abi_version(void) { return 1; }
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or misaligned buffer)";
+    case SA_ERR_UNSUPPORTED: return "unsupported combination (head_dim, block, dtype or size)";
+    case SA_ERR_WORKSPACE: return "workspace smaller than sa_workspace_size";
+    case SA_ERR_HIP: return "HIP launch failed";
+    case SA_ERR_CAPACITY: return "demand union exceeds the packed-buffer capacity";
+  }
+  return "unknown status";
+}
+
+int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes) {
+  Dims g;
+  if (!bytes) return SA_ERR_INVALID_ARG;
+  const int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (stage < SA_STAGE_SELECT || stage > SA_STAGE_FORWARD) return SA_ERR_INVALID_ARG;
+  *bytes = stage_bytes(g, stage);
+  return SA_OK;
+}
+
+int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, const float* wq,
+                       const float* wk, uint32_t* mask_bits, int32_t* row_ptr, int32_t* col_idx,
+                       double* qbar_opt, double* kbar_opt, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (!q || !k || !mask_bits || !row_ptr || !col_idx) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return SA_ERR_INVALID_ARG;
+  if (g.rank > 0 && (!wq || !wk)) return SA_ERR_INVALID_ARG;
+  if ((qbar_opt && ((uintptr_t)qbar_opt & 7u)) || (kbar_opt && ((uintptr_t)kbar_opt & 7u)))
+    return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_SELECT, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SelectWs w = select_ws(g);
+  double* qbar = qbar_opt ? qbar_opt : at<double>(ws, w.qbar);
+  double* kbar = kbar_opt ? kbar_opt : at<double>(ws, w.kbar);
+  double* qt = at<double>(ws, w.qt);
+  double* kt = at<double>(ws, w.kt);
+  double* scores = at<double>(ws, w.scores);
+  int32_t* counts = at<int32_t>(ws, w.counts);
+
+  SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
+  if (g.rank > 0) {
+    SA_TRY_HIP(sa::launch_scores(g, qt, kt, g.rank, 1.0, scores, s));
+  } else {
+    const double sc = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);
+    SA_TRY_HIP(sa::launch_scores(g, qbar, kbar, g.d, sc, scores, s));
+  }
+  SA_TRY_HIP(sa::launch_select(g, scores, prob->select_mode, (double)prob->top_p, prob->top_k,
+                               mask_bits, counts, s));
+  SA_TRY_HIP(sa::launch_csr(g, mask_bits, counts, row_ptr, col_idx, s));
+  return SA_OK;
+}
+
+int sparse_attn_csr_from_mask(const sa_problem* prob, const uint32_t* mask_bits, int32_t* row_ptr,
+                              int32_t* col_idx, void* ws, size_t ws_bytes, void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (!mask_bits || !row_ptr || !col_idx) return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_CSR, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* counts = static_cast<int32_t*>(ws);
+  SA_TRY_HIP(sa::launch_count_bits(g, mask_bits, counts, s));
+  SA_TRY_HIP(sa::launch_csr(g, mask_bits, counts, row_ptr, col_idx, s));
+  return SA_OK;
+}
+
+int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr, const int32_t* col_idx,
+                   const void* k, const void* v, int32_t* demand_ptr, int32_t* demand_idx,
+                   int32_t* col_slot, void* k_packed, void* v_packed, int64_t packed_cap_blocks,
+                   int32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (!row_ptr || !col_idx || !k || !v || !demand_ptr || !demand_idx || !col_slot || !dev_status)
+    return SA_ERR_INVALID_ARG;
+  if (packed_cap_blocks < 0) return SA_ERR_INVALID_ARG;
+  if (packed_cap_blocks > 0 && (!k_packed || !v_packed)) return SA_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_packed) || !aligned16(v_packed))
+    return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_PACK, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PackWs w = pack_ws(g);
+  SA_TRY_HIP(sa::launch_demand(g, row_ptr, col_idx, at<uint32_t>(ws, w.bits),
+                               at<int32_t>(ws, w.heads), demand_ptr, demand_idx, col_slot,
+                               packed_cap_blocks, dev_status, s));
+  SA_TRY_HIP(sa::launch_pack(g, demand_ptr, demand_idx, k, v, k_packed, v_packed,
+                             packed_cap_blocks, s));
+  return SA_OK;
+}
+
+int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* row_ptr,
+                        const int32_t* col_idx, const int32_t* col_slot, const void* k_src,
+                        const void* v_src, void* out, float* lse_opt, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
+  if (!q || !row_ptr || !col_idx || !k_src || !v_src || !out) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(out))
+    return SA_ERR_INVALID_ARG;
+  if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_FORWARD, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* items = static_cast<int32_t*>(ws);
+  const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
+  SA_TRY_HIP(sa::launch_queue(g, row_ptr, items, s));
+  SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, items,
+                             sm, s));
+  return SA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device-side helpers shared by the HIP kernels of the sparse attention path
+// (gfx950, wave64).  Host launchers of every translation unit are declared at
+// the end and called from api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// bf16 <-> fp32 on raw 16-bit patterns (bf16 is the top half of an fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Block-wide reductions and scans over blockDim.x threads (a multiple of 64).
+// `scratch` holds at least blockDim.x/64 elements of T.  Every thread gets the
+// result.  The order of combination is fixed, so results are deterministic.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+template <typename T, typename Op>
+__device__ T block_reduce(T v, T* scratch, Op op) {
+  v = wave_reduce(v, op);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (lane_id() == 0) scratch[w] = v;
+  __syncthreads();
+  T r = scratch[0];
+  for (int i = 1; i < nw; ++i) r = op(r, scratch[i]);
+  return r;
+}
+
+// Inclusive scan within a wave (Hillis-Steele over shuffles).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    T o = __shfl_up(v, off, kWave);
+    if (l >= off) v = v + o;
+  }
+  return v;
+}
+
+// Inclusive block scan; `scratch` >= blockDim.x/64 + 1 elements.  Returns the
+// inclusive prefix for this thread and writes the block total to *total.
+template <typename T>
+__device__ T block_inclusive_scan(T v, T* scratch, T* total) {
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  T inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane_id() == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  T base = T(0), all = T(0);
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) base = base + scratch[i];
+    all = all + scratch[i];
+  }
+  *total = all;
+  return base + inc;
+}
+
+}  // namespace sa
+
+// ---- host launchers (one per translation unit), used by api.hip ----------
+namespace sa {
+struct Dims {
+  int H, d, B, nqb, nkb, W, rank;
+  int64_t q_rows, q_valid, kv_rows, kv_valid;
+  int dtype;
+};
+
+hipError_t launch_pool(const Dims& g, const void* q, const void* k, const float* wq,
+                       const float* wk, double* qbar, double* kbar, double* qt, double* kt,
+                       hipStream_t s);
+hipError_t launch_scores(const Dims& g, const double* qx, const double* kx, int inner,
+                         double scale, double* scores, hipStream_t s);
+hipError_t launch_select(const Dims& g, const double* scores, int mode, double top_p,
+                         int top_k, uint32_t* bits, int32_t* counts, hipStream_t s);
+hipError_t launch_count_bits(const Dims& g, const uint32_t* bits, int32_t* counts,
+                             hipStream_t s);
+hipError_t launch_csr(const Dims& g, const uint32_t* bits, const int32_t* counts,
+                      int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+hipError_t launch_demand(const Dims& g, const int32_t* row_ptr, const int32_t* col_idx,
+                         uint32_t* dem_bits, int32_t* head_count, int32_t* demand_ptr,
+                         int32_t* demand_idx, int32_t* col_slot, int64_t cap,
+                         int32_t* dev_status, hipStream_t s);
+hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* demand_idx,
+                       const void* k, const void* v, void* kp, void* vp, int64_t cap,
+                       hipStream_t s);
+hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s);
+hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
+                       const int32_t* col_idx, const int32_t* col_slot, const void* k,
+                       const void* v, void* out, float* lse, const int32_t* items,
+                       float sm_scale, hipStream_t s);
+}  // namespace sa

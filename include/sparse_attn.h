@@ -1,0 +1,184 @@
+/*
+ * sparse_attn.h -- C ABI of the dynamic block-sparse self-attention path on
+ * one MI355X (gfx950): block pooling -> block scores -> top-p / top-k block
+ * selection -> CSR block lists -> per-head KV demand union and packed gather
+ * -> flash-style attention over the selected blocks only.
+ *
+ * The operation is the one the source pages describe in words:
+ *  - "Dynamic Sparsity in Large-Scale Video DiT Training" (DSV explainer),
+ *    section "The idea": rank query-key pairs with a cheap surrogate (here the
+ *    block means, or a per-head low-rank predictor of inner dimension 16),
+ *    keep the critical ones, let neighbouring queries (one query block) share
+ *    one selected key/value set, and compute attention only on that set with
+ *    kernels that never build the full score matrix.
+ *  - The Top-p sparse-attention abstract (mlsift listing, tag "sequence
+ *    parallelism"): Top-p routing with a Top-k safety floor over blocks of
+ *    video tokens, producing a materialised block mask.
+ *  - "SparSP: Exploiting Communication Sparsity for Sequence-Parallel Video
+ *    DiTs", Abstract: only the KV blocks some query block demands are moved;
+ *    one GPU's part of that is the demand union and its contiguous gather.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless marked (host).  The library never
+ *    allocates, frees, caches or keeps a pointer: the caller owns every
+ *    buffer, including the workspace (size from sa_workspace_size).
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise.  Outputs are ready when the stream is.
+ *  - Q, K, V are contiguous row-major [H, rows, d] with d innermost, rows a
+ *    multiple of the block size B; rows at or beyond the valid count must be
+ *    zero.  Every block holds at least one valid row: rows == ceil(valid/B)*B.
+ *  - Return value: SA_OK (0) or a negative sa_status.  Argument errors are
+ *    detected on the host before any HIP call is made.  A packed-buffer
+ *    overflow, which depends on device data, is reported through the
+ *    `dev_status` word of kv_demand_pack.
+ *  - Identical inputs give bit-identical outputs (no floating-point atomics
+ *    on any output path).
+ *  - Calls on different streams are independent as long as their output and
+ *    workspace buffers do not overlap.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer      */
+  SA_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim/block/dtype mix  */
+  SA_ERR_WORKSPACE = -3,    /* workspace smaller than sa_workspace_size       */
+  SA_ERR_HIP = -4,          /* a HIP launch failed                            */
+  SA_ERR_CAPACITY = -5      /* demand union larger than the packed buffers    */
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+typedef enum sa_select_mode { SA_TOP_P = 0, SA_TOP_K = 1 } sa_select_mode;
+typedef enum sa_score_mode { SA_SCORE_POOLED = 0, SA_SCORE_LOWRANK = 1 } sa_score_mode;
+typedef enum sa_stage {
+  SA_STAGE_SELECT = 0,   /* sparse_attn_select         */
+  SA_STAGE_CSR = 1,      /* sparse_attn_csr_from_mask  */
+  SA_STAGE_PACK = 2,     /* kv_demand_pack             */
+  SA_STAGE_FORWARD = 3   /* sparse_attn_forward        */
+} sa_stage;
+
+/* Problem description (host struct, read during the call only).
+ * Notation: H = num_heads (batch folded in), d = head_dim, B = block,
+ * nQB = q_rows / B, nKB = kv_rows / B, W = ceil(nKB / 32). */
+typedef struct sa_problem {
+  int32_t num_heads;    /* H >= 1                                             */
+  int32_t head_dim;     /* d: 64 or 128 (bf16 attention: 128)                */
+  int32_t block;        /* B: 64 or 128 (bf16 attention: 128); query blocks
+                           and key blocks have the same size                  */
+  int32_t dtype;        /* sa_dtype of Q, K, V, the output and packed K/V     */
+  int64_t q_rows;       /* nQB * B                                            */
+  int64_t q_valid;      /* q_rows - B < q_valid <= q_rows                     */
+  int64_t kv_rows;      /* nKB * B, nKB <= 4096                               */
+  int64_t kv_valid;     /* kv_rows - B < kv_valid <= kv_rows                  */
+  float sm_scale;       /* attention logit scale; <= 0 means 1/sqrt(d)        */
+  float score_scale;    /* pooled block-score scale; <= 0 means 1/sqrt(d)     */
+  int32_t select_mode;  /* sa_select_mode                                     */
+  float top_p;          /* SA_TOP_P: mass to reach, > 0; >= 1 keeps all       */
+  int32_t top_k;        /* SA_TOP_P: floor (>= 0); SA_TOP_K: k (>= 1); both
+                           are clamped to nKB                                 */
+  int32_t score_mode;   /* sa_score_mode                                      */
+  int32_t rank;         /* SA_SCORE_LOWRANK: predictor rank r, 1..64          */
+} sa_problem;
+
+/* Workspace bytes needed by one entry point (`stage`) for this problem.
+ * bytes: host pointer.  The workspace passed to that entry point must be at
+ * least this large and 256-byte aligned; its contents need not be preserved
+ * between calls. */
+int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
+
+/* Pool, score and select (DSV explainer "The idea"; Top-p abstract).
+ *
+ *   qbar[h,i] = mean of the valid rows of query block i   (fp64)
+ *   kbar[h,j] = mean of the valid rows of key block j      (fp64)
+ *   SA_SCORE_POOLED : S[h,i,j] = score_scale * <qbar[h,i], kbar[h,j]>
+ *   SA_SCORE_LOWRANK: S[h,i,j] = <qbar[h,i] Wq[h], kbar[h,j] Wk[h]>, i.e. the
+ *                     mean over the block pair of the rank-r predicted
+ *                     token-pair scores
+ *   SA_TOP_P: P = softmax_j S[h,i,:]; blocks ordered by P descending, ties to
+ *             the lower j; keep the shortest prefix whose cumulative mass
+ *             reaches top_p (all blocks if top_p >= 1 or the prefix never
+ *             reaches it), extended to at least min(top_k, nKB) blocks.
+ *   SA_TOP_K: keep the min(top_k, nKB) largest S, ties to the lower j.
+ * All selection arithmetic is fp64.
+ *
+ * q [H,q_rows,d], k [H,kv_rows,d]: input dtype.
+ * wq, wk: fp32 [H,d,rank] (SA_SCORE_LOWRANK only; else ignored, may be NULL).
+ * mask_bits: out, uint32 [H*nQB, W]; bit b of word w of row h*nQB+i is block
+ *            32w+b; bits at or beyond nKB are 0.
+ * row_ptr:   out, int32 [H*nQB+1], CSR row offsets (rows head-major).
+ * col_idx:   out, int32, capacity H*nQB*nKB; entries of a row ascending.
+ * qbar_opt, kbar_opt: NULL or out fp64 [H,nQB,d] / [H,nKB,d].
+ * ws: workspace of sa_workspace_size(SA_STAGE_SELECT) bytes. */
+int sparse_attn_select(const sa_problem* prob, const void* q, const void* k,
+                       const float* wq, const float* wk, uint32_t* mask_bits,
+                       int32_t* row_ptr, int32_t* col_idx, double* qbar_opt,
+                       double* kbar_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* CSR of an externally given (for example repaired) block mask, the same
+ * layout sparse_attn_select writes (Top-p abstract: the materialised mask).
+ * mask_bits: in, uint32 [H*nQB, W] (bits beyond nKB are ignored).
+ * row_ptr: out [H*nQB+1]; col_idx: out, capacity H*nQB*nKB. */
+int sparse_attn_csr_from_mask(const sa_problem* prob, const uint32_t* mask_bits,
+                              int32_t* row_ptr, int32_t* col_idx, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Per-head KV demand union and packed gather (SparSP Abstract:
+ * demand-directed KV routing; this is one GPU's share of it).
+ *
+ *   demanded[h] = union over the query blocks i of head h of their blocks
+ *   demand_ptr [H+1]: out, head h owns slots demand_ptr[h] .. demand_ptr[h+1]-1
+ *   demand_idx: out, capacity H*nKB; block id of each slot, ascending in a head
+ *   col_slot:   out, capacity H*nQB*nKB; slot of each CSR entry
+ *   k_packed, v_packed: out, [packed_cap_blocks, B, d] in the input dtype;
+ *               slot s holds a bitwise copy of rows j*B .. j*B+B-1 of head h
+ * row_ptr, col_idx: a CSR as written by the calls above.
+ * dev_status: out, int32 [1]: 0, or SA_ERR_CAPACITY when the union exceeds
+ *             packed_cap_blocks (then only the first packed_cap_blocks slots
+ *             are copied; demand_ptr, demand_idx and col_slot are complete).
+ * packed_cap_blocks >= 0. */
+int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr,
+                   const int32_t* col_idx, const void* k, const void* v,
+                   int32_t* demand_ptr, int32_t* demand_idx, int32_t* col_slot,
+                   void* k_packed, void* v_packed, int64_t packed_cap_blocks,
+                   int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention over the selected blocks only (DSV explainer "The idea": sparse
+ * attention kernels that never build the full score matrix).
+ *
+ * For query a of block i of head h and key b of a selected block j:
+ *   z = sm_scale * <q_a, k_b>, with keys b >= kv_valid excluded;
+ *   out[h,a] = sum_b softmax(z)_b v_b,  lse[h,a] = ln sum_b exp(z_b).
+ * Query rows a >= q_valid, and rows whose block selected nothing, get out = 0
+ * and lse = -inf.  bf16 inputs use bf16 MFMA with fp32 accumulation; the
+ * output has the input dtype (round to nearest even), lse is fp32.
+ *
+ * col_slot == NULL: k_src, v_src are the full K, V [H,kv_rows,d].
+ * col_slot != NULL: k_src, v_src are packed [slots,B,d] and entry e reads
+ *                   slot col_slot[e] (col_idx still gives the block id).
+ * Work items (head, query block) are processed longest-first.
+ * out: [H,q_rows,d] input dtype; lse_opt: NULL or fp32 [H,q_rows]. */
+int sparse_attn_forward(const sa_problem* prob, const void* q,
+                        const int32_t* row_ptr, const int32_t* col_idx,
+                        const int32_t* col_slot, const void* k_src,
+                        const void* v_src, void* out, float* lse_opt, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* sa_status_string(int status);
+
+/* ABI version of this header: 1. */
+int sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,153 @@
+"""C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any HIP
+call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_scores_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("library not built (python -m block_sparse_attention_scores_amd.build)")
+    return B.load()
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for name in B.EXPORTS:
+        assert name in fns
+    assert set(fns) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.sa_abi_version() == 1
+
+
+def test_struct_layout_matches_c():
+    # int32 x4, int64 x4, float x2, int32, float, int32 x3 -> 76 bytes, padded to 80
+    assert ctypes.sizeof(B.SaProblem) == 80
+    assert B.SaProblem.q_rows.offset == 16 and B.SaProblem.sm_scale.offset == 48
+    assert B.SaProblem.rank.offset == 72
+
+
+def good_problem(**kw):
+    p = dict(heads=2, head_dim=128, block=128, dtype=B.SA_BF16, q_rows=512, q_valid=500,
+             kv_rows=1024, kv_valid=1000, top_p=0.9, top_k=4)
+    p.update(kw)
+    return B.problem(**p)
+
+
+def status_of_ws(prob, stage=B.SA_STAGE_SELECT):
+    n = ctypes.c_size_t(0)
+    return B.load().sa_workspace_size(ctypes.byref(prob), stage, ctypes.byref(n)), n.value
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert B.status_string(s)
+    assert B.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    st, n = status_of_ws(good_problem())
+    assert st == 0
+    H, nqb, nkb, d = 2, 4, 8, 128
+    assert n >= 8 * (H * nqb * d + H * nkb * d + H * nqb * nkb) + 4 * H * nqb
+    for stage in (B.SA_STAGE_CSR, B.SA_STAGE_PACK, B.SA_STAGE_FORWARD):
+        st, n = status_of_ws(good_problem(), stage)
+        assert st == 0 and n > 0 and n % 256 == 0
+    assert status_of_ws(good_problem(), 9)[0] == B.SA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(heads=0), B.SA_ERR_INVALID_ARG),
+    (dict(head_dim=96), B.SA_ERR_UNSUPPORTED),
+    (dict(block=32), B.SA_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.SA_ERR_INVALID_ARG),
+    (dict(q_rows=500), B.SA_ERR_INVALID_ARG),            # not a multiple of the block
+    (dict(q_valid=384), B.SA_ERR_INVALID_ARG),           # a block without valid rows
+    (dict(q_valid=513), B.SA_ERR_INVALID_ARG),
+    (dict(kv_valid=0), B.SA_ERR_INVALID_ARG),
+    (dict(kv_rows=128 * 4097, kv_valid=128 * 4097), B.SA_ERR_UNSUPPORTED),
+    (dict(top_p=0.0), B.SA_ERR_INVALID_ARG),
+    (dict(top_k=-1), B.SA_ERR_INVALID_ARG),
+    (dict(select_mode=B.SA_TOP_K, top_k=0), B.SA_ERR_INVALID_ARG),
+    (dict(select_mode=5), B.SA_ERR_INVALID_ARG),
+    (dict(score_mode=B.SA_SCORE_LOWRANK, rank=0), B.SA_ERR_INVALID_ARG),
+    (dict(score_mode=B.SA_SCORE_LOWRANK, rank=65), B.SA_ERR_INVALID_ARG),
+    (dict(sm_scale=float("nan")), B.SA_ERR_INVALID_ARG),
+])
+def test_problem_validation(lib, kw, expect):
+    assert status_of_ws(good_problem(**kw))[0] == expect
+
+
+FAKE = 1 << 20            # never dereferenced: every call below fails validation first
+
+
+def test_select_argument_errors(lib):
+    p = good_problem()
+    st, n = status_of_ws(p)
+    f = lib.sparse_attn_select
+    args = [ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, FAKE * 4, n, None]
+    bad = list(args); bad[1] = None
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # null q
+    bad = list(args); bad[2] = FAKE + 2
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # misaligned k
+    bad = list(args); bad[10] = FAKE * 4 + 64
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # workspace not 256-aligned
+    bad = list(args); bad[11] = n - 1
+    assert f(*bad) == B.SA_ERR_WORKSPACE                       # workspace too small
+    lr = good_problem(score_mode=B.SA_SCORE_LOWRANK, rank=16)
+    bad = list(args); bad[0] = ctypes.byref(lr)
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # low-rank without W
+
+
+def test_pack_and_forward_argument_errors(lib):
+    p = good_problem()
+    _, n = status_of_ws(p, B.SA_STAGE_PACK)
+    f = lib.kv_demand_pack
+    args = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE,
+            FAKE * 4, n, None]
+    bad = list(args); bad[10] = -1
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # negative capacity
+    bad = list(args); bad[8] = None
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # capacity > 0, no buffer
+    bad = list(args); bad[11] = None
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # no status word
+    bad = list(args); bad[13] = 0
+    assert f(*bad) == B.SA_ERR_WORKSPACE
+
+    _, n = status_of_ws(p, B.SA_STAGE_FORWARD)
+    f = lib.sparse_attn_forward
+    args = [ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE * 4, n, None]
+    bad = list(args); bad[7] = None
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # no output
+    bad = list(args); bad[8] = FAKE + 2
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # misaligned lse
+    q64 = good_problem(head_dim=64, block=64, q_rows=256, q_valid=256, kv_rows=256, kv_valid=256)
+    bad = list(args); bad[0] = ctypes.byref(q64)
+    assert f(*bad) == B.SA_ERR_UNSUPPORTED                     # bf16 attention needs d=B=128
+
+
+def test_csr_argument_errors(lib):
+    p = good_problem()
+    _, n = status_of_ws(p, B.SA_STAGE_CSR)
+    f = lib.sparse_attn_csr_from_mask
+    assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE * 4, 0, None) == B.SA_ERR_WORKSPACE
+    assert f(None, FAKE, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
