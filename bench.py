@@ -1,0 +1,210 @@
+"""Benchmark of the block-sparse attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 480p]
+
+One step = one pass of the whole path over one synthetic layer resident in
+HBM: sparse_attn_select (pool, score, top-p/top-k, CSR) -> kv_demand_pack
+(demand union, packed gather) -> sparse_attn_forward (work queue, attention
+over the selected blocks).  Every stage is timed with HIP events on the
+stream the library launches on; L2 and the Infinity Cache are flushed
+(512 MiB write) before each step, outside the events.
+
+Prints ONE JSON line.  ``value`` is selected-block attention TFLOP/s of the
+whole step, 4*B^2*d*nnz / step time; ``roofline`` is that of the dominant
+kernel (the attention forward, bf16 MFMA).  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc", "attn_fwd.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="480p", help="tiny | 480p | 720p_rank | lowrank | hetero")
+    ap.add_argument("--unpacked", action="store_true", help="attend straight from K/V (no pack)")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-items", type=int, default=256,
+                    help="(head, query block) items in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(config_name, nnz):
+    """HBM bytes per attention launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    only if they were taken on the current kernel source and workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(config_name)
+    if not r or r.get("source_sha256") != source_digest(ATTN_SOURCE) or r.get("nnz") != nnz:
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, n_items):
+    """The oracle, as it stands, on a bounded sample: selection, CSR/demand/pack
+    for every row (pro-rated by the item fraction) and dense masked attention
+    for ``n_items`` randomly chosen (head, query block) items."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import oracle as O
+
+    t0 = time.perf_counter()
+    _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
+                           w.eff_score_scale, x.get("wq"), x.get("wk"))
+    mask, _ = O.select(s, w.select_mode, w.top_p, w.top_k)
+    rp, ci = O.csr(mask)
+    dp, di, _, _ = O.demand(mask, rp, ci)
+    O.pack(x["k"], dp, di, w.block)
+    O.pack(x["v"], dp, di, w.block)
+    t_sel = time.perf_counter() - t0
+    rows = w.heads * w.n_qb
+    n_items = min(n_items, rows)
+    pick = np.random.default_rng(0).choice(rows, size=n_items, replace=False)
+    items = [(int(r) // w.n_qb, int(r) % w.n_qb) for r in sorted(pick)]
+    t0 = time.perf_counter()
+    O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block, w.eff_sm_scale,
+                items=items)
+    t_att = time.perf_counter() - t0
+    nnz_sample = int(sum(mask[h, i].sum() for h, i in items))
+    t = t_att + t_sel * n_items / rows
+    flops = 4.0 * w.block * w.block * w.head_dim * nnz_sample
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{n_items} of {rows} (head, query-block) items of {w.name}: dense fp32 "
+                       f"masked attention for the sample ({t_att:.2f} s) + fp64 selection, CSR, "
+                       f"demand and pack of all rows ({t_sel:.2f} s) pro-rated by "
+                       f"{n_items}/{rows}"),
+            "seconds": round(t_att + t_sel, 3), "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_sparse_attention_scores_amd import binding, inputs as I
+    from block_sparse_attention_scores_amd.path import SparseAttention, to_device
+
+    binding.load()                       # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    w = I.named(args.config)
+    x = I.generate(w)
+    d = to_device(x, w)
+    sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
+    packed = not args.unpacked
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        ev[0].record()
+        sa.select()
+        ev[1].record()
+        if packed:
+            sa.pack()
+        ev[2].record()
+        sa.forward(packed=packed)
+        ev[3].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xff)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    sel = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pck = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    fwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    tot = sel + pck + fwd
+    nnz = sa.nnz()
+    dense_pairs = w.heads * w.n_qb * w.n_kb
+    flops = 4.0 * w.block * w.block * w.head_dim * nnz
+    ms_step = float(tot.mean())
+    eb = 2 if w.dtype == "bf16" else 4
+    demand = int(sa.demand_ptr[-1].item())
+    sel_bytes = w.heads * (w.q_rows + w.kv_rows) * w.head_dim * eb
+    pack_bytes = 2 * 2 * demand * w.block * w.head_dim * eb
+    fwd_ms = float(fwd.mean())
+    achieved = flops / (fwd_ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = load_traffic(w.name, nnz)
+
+    rec = {
+        "metric": "block-sparse attn TFLOP/s (selected blocks) + ms/layer @32k tokens, 1 MI355X",
+        "value": round(flops / (ms_step / 1e3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded clustered video-latent Q/K, N(0,1) V)",
+        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
+                   "block": w.block, "q_tokens": w.q_valid, "kv_tokens": w.kv_valid,
+                   "latent_thw": list(w.latent), "top_p": w.top_p, "top_k": w.top_k,
+                   "select_mode": "top_p" if w.select_mode == 0 else "top_k",
+                   "score": "pooled" if w.score_mode == 0 else f"lowrank{w.rank}",
+                   "packed_kv": packed, "cache": "warm" if flush is None else "flushed each step"},
+        "ms_per_layer": round(ms_step, 4),
+        "stages_ms": {"select": round(float(sel.mean()), 4), "pack": round(float(pck.mean()), 4),
+                      "forward": round(fwd_ms, 4),
+                      "forward_p10_p90": [round(float(np.percentile(fwd, 10)), 4),
+                                          round(float(np.percentile(fwd, 90)), 4)]},
+        "selected_blocks": nnz, "dense_blocks": dense_pairs,
+        "selected_fraction": round(nnz / dense_pairs, 4),
+        "demanded_blocks": demand, "selected_tflop": round(flops / 1e12, 4),
+        "stage_roofline": {
+            "select_hbm_frac": round(sel_bytes / (float(sel.mean()) / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "pack_hbm_frac": (round(pack_bytes / (float(pck.mean()) / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
+                              if packed else None),
+            "select_bytes": sel_bytes, "pack_bytes": pack_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "sparse_attn_forward (work-queue sort + attention)"},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,10 +160,96 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
 // bf16 MFMA path, d = 128, block = 128
 // ---------------------------------------------------------------------------
 constexpr int kD = 128, kB = 128;
-constexpr int kKsStride = kD + 8;   // K tile row stride in bf16 (272 bytes)
-constexpr int kVtStride = kB + 8;   // V^T tile row stride in bf16 (272 bytes)
+constexpr int kKsStride = kD + 8;   // K tile row stride in bf16 (272 B: 16-B reads conflict-free)
+constexpr int kVtStride = kB + 4;   // V^T tile row stride in bf16 (264 B = 66 dwords)
+constexpr int kTileBytes = kB * kD * 2;
 
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer, 32-bit dword data format (gfx9 CDNA descriptor word 3)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// 8 consecutive fp32 accumulator values -> bf16x8 (v_cvt_pk_bf16_f32, RNE)
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int base) {
+  f32x8 v;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) v[x] = a[base + x];
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// (a.lo, b.lo) and (a.hi, b.hi): 16-bit halves of two rows interleaved
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Staging of one K/V block pair (global -> registers -> LDS).
+//  K: 16-byte chunk c16 = tid + 256*it (it < 8): row c16 >> 4, column chunk c16 & 15;
+//     global reads fully coalesced, LDS rows padded to 272 B.
+//  V: 4 keys x 8 d per thread and iteration (it < 2).  In a wave, lanes l give
+//     key group kg = (l & 15) + 16*(c & 1) and d chunk dc = (l >> 4) + 4*(c >> 1),
+//     c = wave + 4*it; 16 consecutive lanes hold 16 different key groups, so the
+//     transposed 8-byte writes V^T[d][4kg..4kg+3] of those lanes fall in 32
+//     distinct banks (row stride 66 dwords).
+struct Stage {
+  u32x4 k[8];
+  u32x4 v[2][4];
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* kb, const uint16_t* vb,
+                                           int tid, int wave) {
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, kTileBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, kTileBytes);
+  const int koff = (tid >> 4) * 256 + (tid & 15) * 16;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) st.k[it] = buf_load16(rk, koff, it * 4096);
+  const int l = tid & 63;
+  const int voff = (4 * (l & 15)) * 256 + (l >> 4) * 16;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int c = wave + 4 * it;
+    const int base = (64 * (c & 1)) * 256 + (4 * (c >> 1)) * 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.v[it][r] = buf_load16(rv, voff, base + r * 256);
+  }
+}
+
+__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* ks, uint16_t* vt, int tid,
+                                            int wave) {
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    *reinterpret_cast<u32x4*>(ks + ((tid >> 4) + 16 * it) * kKsStride + (tid & 15) * 8) = st.k[it];
+  const int l = tid & 63;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int c = wave + 4 * it;
+    const int kg = (l & 15) + 16 * (c & 1);
+    const int dc = (l >> 4) + 4 * (c >> 1);
+    uint16_t* dst = vt + (8 * dc) * kVtStride + 4 * kg;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      u32x2 lo, hi;   // d = 8dc + 2cc (low halves) and 8dc + 2cc + 1 (high halves)
+      lo.x = pack_lo(st.v[it][0][cc], st.v[it][1][cc]);
+      lo.y = pack_lo(st.v[it][2][cc], st.v[it][3][cc]);
+      hi.x = pack_hi(st.v[it][0][cc], st.v[it][1][cc]);
+      hi.y = pack_hi(st.v[it][2][cc], st.v[it][3][cc]);
+      *reinterpret_cast<u32x2*>(dst + (2 * cc) * kVtStride) = lo;
+      *reinterpret_cast<u32x2*>(dst + (2 * cc + 1) * kVtStride) = hi;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ col_slot,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
@@ -172,18 +258,21 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks[kB * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lq = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
   const int item = items[blockIdx.x];
   const int h = item / nqb, i = item % nqb;
-  const int64_t qrow = (int64_t)i * kB + 32 * wave + lq;   // this lane's query row
+  const int qloc = 32 * wave + lq;                                // query row within the block
 
   // Q fragments (B operand of S^T = K Q^T): d = 16s + 8g .. +8
   bf16x8 qf[8];
   {
-    const uint16_t* qp = q + ((int64_t)h * q_rows + qrow) * kD + 8 * g;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(q + ((int64_t)h * q_rows + (int64_t)i * kB) * kD, kTileBytes);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int s = 0; s < 8; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, qloc * 256 + 16 * g, 32 * s));
   }
 
   f32x16 oacc[4];
@@ -194,63 +283,29 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   const int e0 = row_ptr[item], e1 = row_ptr[item + 1];
-  for (int e = e0; e < e1; ++e) {
+  // source block of entry e (-1: skip)
+  auto block_of = [&](int e) -> int64_t {
     const int j = col_idx[e];
-    int64_t blk;
-    if (col_slot) {
-      blk = col_slot[e];
-      if (blk < 0) continue;
-    } else {
-      if ((unsigned)j >= (unsigned)nkb) continue;
-      blk = (int64_t)h * nkb + j;
-    }
-    const uint16_t* kb = k + blk * (kB * kD);
-    const uint16_t* vb = v + blk * (kB * kD);
+    if ((unsigned)j >= (unsigned)nkb) return -1;
+    return col_slot ? (int64_t)col_slot[e] : (int64_t)h * nkb + j;
+  };
 
-    // global -> registers: K as 8 x 16 B row chunks, V as 2 x (4 rows x 8 d)
-    uint4 kr[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c16 = tid + 256 * it;
-      kr[it] = *reinterpret_cast<const uint4*>(kb + (c16 >> 4) * kD + (c16 & 15) * 8);
-    }
-    uint4 vr[2][4];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int sub = tid + 256 * it, dc = sub & 15, kg = sub >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[it][r] = *reinterpret_cast<const uint4*>(vb + (4 * kg + r) * kD + 8 * dc);
-    }
-    __syncthreads();   // everyone is done reading the previous tiles
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c16 = tid + 256 * it;
-      *reinterpret_cast<uint4*>(ks + (c16 >> 4) * kKsStride + (c16 & 15) * 8) = kr[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int sub = tid + 256 * it, dc = sub & 15, kg = sub >> 4;
-      const int kgs = kg ^ dc;   // swizzle: d >> 3 == dc for these 8 rows
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[it][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[it][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[it][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[it][3]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int c = x >> 1;
-        uint2 pr;
-        if (x & 1) {
-          pr.x = (w0[c] >> 16) | (w1[c] & 0xffff0000u);
-          pr.y = (w2[c] >> 16) | (w3[c] & 0xffff0000u);
-        } else {
-          pr.x = (w0[c] & 0xffffu) | (w1[c] << 16);
-          pr.y = (w2[c] & 0xffffu) | (w3[c] << 16);
-        }
-        *reinterpret_cast<uint2*>(vt + (8 * dc + x) * kVtStride + 4 * kgs) = pr;
-      }
-    }
+  Stage st;
+  int e = e0;
+  int64_t blk = -1;
+  while (e < e1 && (blk = block_of(e)) < 0) ++e;
+  if (e < e1) stage_load(st, k + blk * (kB * kD), v + blk * (kB * kD), tid, wave);
+
+  while (e < e1) {
+    const int j = col_idx[e];
+    __syncthreads();                 // all waves are done reading the previous tiles
+    stage_store(st, ks, vt, tid, wave);
     __syncthreads();
+    // prefetch the next block while this one is computed
+    int en = e + 1;
+    int64_t bn = -1;
+    while (en < e1 && (bn = block_of(en)) < 0) ++en;
+    if (en < e1) stage_load(st, k + bn * (kB * kD), v + bn * (kB * kD), tid, wave);
 
     // S^T tile t: keys 32t.., this lane's query; reg r -> key 32t + 8(r/4) + 4g + r%4
     f32x16 sacc[4];
@@ -266,18 +321,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
       }
     }
 
-    const int64_t lim = kv_valid - (int64_t)j * kB;   // keys >= lim are padding
+    const int lim = (int)min((int64_t)kB, kv_valid - (int64_t)j * kB);   // valid keys
     float mx = -INFINITY;
+    if (lim < kB) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kk >= lim) sacc[t][r] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float x = (kk < lim) ? sacc[t][r] * scale_log2 : -INFINITY;
-        sacc[t][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     const float mn = fmaxf(m_run, mx);
     const float alpha = exp2f(m_run - mn);
     m_run = mn;
@@ -286,44 +345,40 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sacc[t][r] - mn);
+        const float p = exp2f(fmaf(sacc[t][r], scale_log2, -mn));
         sacc[t][r] = p;
         ps += p;
       }
-    l_run = l_run * alpha + ps;
+    l_run = fmaf(l_run, alpha, ps);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
 
-    // O^T += V^T P^T; k-step (t, h2) covers keys 32t + 16h2 .. +16
+    // O^T += V^T P^T; k-step (t, h2) covers keys 32t + 16h2 .. +16: slots 0-3 are
+    // keys 4*kga .. +3 and slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          pw[x] = pack_bf16x2(sacc[t][8 * h2 + 2 * x], sacc[t][8 * h2 + 2 * x + 1]);
-        bf16x8 pf;
-        __builtin_memcpy(&pf, pw, 16);
-        const int kga = 8 * t + 4 * h2 + g, kgb = kga + 2;
+        const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
+        const int kga = 8 * t + 4 * h2 + g;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int d = 32 * u + lq;
-          const int sw = (d >> 3) & 15;
-          const uint2 va = *reinterpret_cast<const uint2*>(vt + d * kVtStride + 4 * (kga ^ sw));
-          const uint2 vb2 = *reinterpret_cast<const uint2*>(vt + d * kVtStride + 4 * (kgb ^ sw));
-          const uint32_t vw[4] = {va.x, va.y, vb2.x, vb2.y};
-          bf16x8 vf;
-          __builtin_memcpy(&vf, vw, 16);
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[u], 0, 0, 0);
+          const uint16_t* vrow = vt + (32 * u + lq) * kVtStride;
+          const u32x2 va = *reinterpret_cast<const u32x2*>(vrow + 4 * kga);
+          const u32x2 vb2 = *reinterpret_cast<const u32x2*>(vrow + 4 * (kga + 2));
+          const u32x4 vw = {va.x, va.y, vb2.x, vb2.y};
+          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
+                                                            oacc[u], 0, 0, 0);
         }
       }
     }
+    e = en;
   }
 
   // finalise: O[query][d], reg r of d-tile u -> d = 32u + 8(r/4) + 4g + r%4
+  const int64_t qrow = (int64_t)i * kB + qloc;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const bool live = qrow < q_valid && l_tot > 0.f;
   const float inv = live ? 1.f / l_tot : 0.f;
@@ -332,10 +387,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      uint2 w;
-      w.x = pack_bf16x2(oacc[u][4 * r4 + 0] * inv, oacc[u][4 * r4 + 1] * inv);
-      w.y = pack_bf16x2(oacc[u][4 * r4 + 2] * inv, oacc[u][4 * r4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + 32 * u + 8 * r4 + 4 * g) = w;
+      f32x4 o4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o4[x] = oacc[u][4 * r4 + x] * inv;
+      *reinterpret_cast<bf16x4*>(op + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(o4, bf16x4);
     }
   if (lse && g == 0)
     lse[(int64_t)h * q_rows + qrow] =
