@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-items", type=int, default=256,
                     help="(head, query block) items in the oracle's timed sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before warmup, run one plain device copy of MIB MiB (untimed), the "
+                         "known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -134,6 +137,14 @@ def main():
         ev[2].record()
         sa.forward(packed=packed)
         ev[3].record()
+
+    if args.copy_probe > 0:
+        src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for _ in range(args.warmup):

@@ -61,11 +61,13 @@ class SparseAttnError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load the HIP library (once).  Raises if it has not been built."""
+def load(path: str = None):
+    """Load the HIP library (once).  Raises if it has not been built.
+    ``SA_LIBRARY`` in the environment names another build of the same ABI."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m block_sparse_attention_scores_amd.build`")

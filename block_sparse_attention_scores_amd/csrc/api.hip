@@ -8,6 +8,7 @@
 
 namespace sa {
 bool attn_supported(int dtype, int d, int B);
+int queue_words(int rows);
 }
 
 namespace {
@@ -87,7 +88,7 @@ PackWs pack_ws(const Dims& g) {
   w.total = o;
   return w;
 }
-size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * g.H * g.nqb); }
+size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * sa::queue_words(g.H * g.nqb)); }
 
 size_t stage_bytes(const Dims& g, int stage) {
   switch (stage) {

@@ -24,6 +24,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -32,46 +34,81 @@ namespace {
 // ---------------------------------------------------------------------------
 // work queue
 // ---------------------------------------------------------------------------
+// Items (head, query block) are split into kXcd contiguous ranges of the
+// head-major item order, balanced by selected-block count (the work), one
+// range per XCD: concurrent workgroups of an XCD then attend to the same
+// head's key/value blocks, which stay resident in that XCD's L2.  Inside a
+// range, items go longest first.  A counting sort on (range, count) writes
+// the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here) is its cursor.
+constexpr int kXcd = 8;
 constexpr int kQueueThreads = 1024;
-constexpr int kQueueMax = 32768;
+constexpr int kQueueMaxBins = kXcd * (4096 + 1);
 
-__global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __restrict__ row_ptr,
-                                                              int rows, int nkb, int n2,
-                                                              int idbits,
-                                                              int32_t* __restrict__ items) {
-  __shared__ uint32_t key[kQueueMax];
-  const int t = threadIdx.x;
-  const uint32_t idmask = (1u << idbits) - 1u;
-  for (int r = t; r < n2; r += kQueueThreads) {
-    if (r < rows) {
-      const uint32_t c = (uint32_t)(row_ptr[r + 1] - row_ptr[r]);
-      key[r] = (((uint32_t)nkb - min(c, (uint32_t)nkb)) << idbits) | (uint32_t)r;
-    } else {
-      key[r] = 0xffffffffu;
-    }
-  }
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = t; p < (n2 >> 1); p += kQueueThreads) {
-        const int a = 2 * stride * (p / stride) + (p % stride);
-        const int b = a + stride;
-        const uint32_t ka = key[a], kb = key[b];
-        const bool up = (a & size) == 0;
-        if ((ka > kb) == up) {
-          key[a] = kb;
-          key[b] = ka;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int r = t; r < rows; r += kQueueThreads) items[r] = (int32_t)(key[r] & idmask);
+__device__ __forceinline__ int queue_key(const int32_t* row_ptr, int r, int nkb, int64_t total) {
+  const int c = row_ptr[r + 1] - row_ptr[r];
+  const int64_t mid = (int64_t)row_ptr[r] + c / 2;
+  const int x = total > 0 ? (int)min<int64_t>(kXcd - 1, mid * kXcd / total) : 0;
+  return x * (nkb + 1) + (nkb - min(c, nkb));
 }
 
-__global__ void identity_queue_kernel(int rows, int32_t* __restrict__ items) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r < rows) items[r] = r;
+__global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __restrict__ row_ptr,
+                                                              int rows, int nkb,
+                                                              int32_t* __restrict__ items,
+                                                              int32_t* __restrict__ xq,
+                                                              int32_t* __restrict__ ctr) {
+  __shared__ int hist[kQueueMaxBins];
+  __shared__ int red[kQueueThreads / kWave + 1];
+  const int t = threadIdx.x;
+  const int nb = kXcd * (nkb + 1);
+  const int64_t total = row_ptr[rows];
+  for (int b = t; b < nb; b += kQueueThreads) hist[b] = 0;
+  __syncthreads();
+  for (int r = t; r < rows; r += kQueueThreads) atomicAdd(&hist[queue_key(row_ptr, r, nkb, total)], 1);
+  __syncthreads();
+  // exclusive scan of the histogram, contiguous chunk per thread
+  const int per = (nb + kQueueThreads - 1) / kQueueThreads;
+  const int lo = min(nb, t * per), hi = min(nb, lo + per);
+  int local = 0;
+  for (int b = lo; b < hi; ++b) local += hist[b];
+  int all;
+  int run = block_inclusive_scan(local, red, &all) - local;
+  __syncthreads();
+  for (int b = lo; b < hi; ++b) {
+    const int c = hist[b];
+    hist[b] = run;
+    run += c;
+  }
+  __syncthreads();
+  if (t < kXcd) {
+    xq[t] = hist[t * (nkb + 1)];
+    ctr[t] = 0;
+  }
+  if (t == 0) xq[kXcd] = rows;
+  __syncthreads();
+  // scatter; the order among items with equal (range, count) is immaterial
+  for (int r = t; r < rows; r += kQueueThreads)
+    items[atomicAdd(&hist[queue_key(row_ptr, r, nkb, total)], 1)] = r;
+}
+
+// Next item for a persistent workgroup: its own XCD's range first, then the
+// others' (stealing).  -1 when every range is exhausted.
+__device__ __forceinline__ int pop_item(const int32_t* __restrict__ items,
+                                        const int32_t* __restrict__ xq, int32_t* ctr, int home) {
+  for (int k = 0; k < kXcd; ++k) {
+    const int x = (home + k) & (kXcd - 1);
+    const int n = xq[x + 1] - xq[x];
+    if (n <= 0) continue;
+    if (__hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    const int idx = atomicAdd(&ctr[x], 1);
+    if (idx < n) return items[xq[x] + idx];
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int xcc_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & (kXcd - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -206,8 +243,18 @@ struct Stage {
   u32x4 v[2][4];
 };
 
+// The lane offsets below are recomputed from the thread id at every use (the
+// empty asm makes the id opaque, so it is not hoisted out of the loop): cheaper
+// than keeping them live across the loop, which spills at 256 registers.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ void stage_load(Stage& st, const uint16_t* kb, const uint16_t* vb,
-                                           int tid, int wave) {
+                                           int /*tid*/, int wave) {
+  const int tid = opaque_tid();
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, kTileBytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, kTileBytes);
   const int koff = (tid >> 4) * 256 + (tid & 15) * 16;
@@ -224,8 +271,9 @@ __device__ __forceinline__ void stage_load(Stage& st, const uint16_t* kb, const 
   }
 }
 
-__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* ks, uint16_t* vt, int tid,
-                                            int wave) {
+__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* ks, uint16_t* vt,
+                                            int /*tid*/, int wave) {
+  const int tid = opaque_tid();
 #pragma unroll
   for (int it = 0; it < 8; ++it)
     *reinterpret_cast<u32x4*>(ks + ((tid >> 4) + 16 * it) * kKsStride + (tid & 15) * 8) = st.k[it];
@@ -249,19 +297,16 @@ __device__ __forceinline__ void stage_store(const Stage& st, uint16_t* ks, uint1
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ col_slot,
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-    float* __restrict__ lse, const int32_t* __restrict__ items, int nqb, int nkb,
-    int64_t q_rows, int64_t q_valid, int64_t kv_rows, int64_t kv_valid, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kB * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];
-
+// One (head, query block) item by one workgroup of four waves.
+__device__ __forceinline__ void attend_item(
+    int item, uint16_t* ks, uint16_t* vt, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ col_slot, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_valid, float scale_log2) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
-  const int item = items[blockIdx.x];
   const int h = item / nqb, i = item % nqb;
   const int qloc = 32 * wave + lq;                                // query row within the block
 
@@ -282,12 +327,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     for (int r = 0; r < 16; ++r) oacc[u][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int e0 = row_ptr[item], e1 = row_ptr[item + 1];
+  // every value below is uniform across the workgroup; readfirstlane keeps it
+  // in scalar registers (buffer descriptors need them)
+  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[item]);
+  const int e1 = __builtin_amdgcn_readfirstlane(row_ptr[item + 1]);
   // source block of entry e (-1: skip)
   auto block_of = [&](int e) -> int64_t {
-    const int j = col_idx[e];
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
     if ((unsigned)j >= (unsigned)nkb) return -1;
-    return col_slot ? (int64_t)col_slot[e] : (int64_t)h * nkb + j;
+    return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(col_slot[e]) : (int64_t)h * nkb + j;
   };
 
   Stage st;
@@ -297,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   if (e < e1) stage_load(st, k + blk * (kB * kD), v + blk * (kB * kD), tid, wave);
 
   while (e < e1) {
-    const int j = col_idx[e];
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
     __syncthreads();                 // all waves are done reading the previous tiles
     stage_store(st, ks, vt, tid, wave);
     __syncthreads();
@@ -321,16 +369,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       }
     }
 
-    const int lim = (int)min((int64_t)kB, kv_valid - (int64_t)j * kB);   // valid keys
+    // valid keys of this block (uniform); only the sequence's last block is ragged
+    const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
     float mx = -INFINITY;
-    if (lim < kB) {
+    if (__builtin_expect(lim < kB, 0)) {
+      const int lim_g = lim - 4 * g;   // key 32t + 8(r/4) + 4g + r%4 >= lim
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kk >= lim) sacc[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + (r & 3) >= lim_g) sacc[t][r] = -INFINITY;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -338,27 +386,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     const float mn = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - mn);
+    // v_exp_f32 directly: masses below 2^-126 flush to 0, which softmax tolerates
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+    // rescale O only if some query's running max moved (wave-uniform branch)
+    if (__ballot(m_run != mn)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+    }
+    l_run *= alpha;
     m_run = mn;
+
+    // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
+    // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
+    // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g.  The exp of tile t+1
+    // is independent of the MFMAs of tile t, so the two can overlap.
     float ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(sacc[t][r], scale_log2, -mn));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -mn));
         sacc[t][r] = p;
         ps += p;
       }
-    l_run = fmaf(l_run, alpha, ps);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-
-    // O^T += V^T P^T; k-step (t, h2) covers keys 32t + 16h2 .. +16: slots 0-3 are
-    // keys 4*kga .. +3 and slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
@@ -374,6 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         }
       }
     }
+    l_run += ps;
     e = en;
   }
 
@@ -397,6 +450,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         live ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Persistent: each workgroup pops items from its XCD's queue until all queues
+// are empty (every workgroup reaches that exit; no workgroup waits on another).
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ col_slot,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+    float* __restrict__ lse, const int32_t* __restrict__ items, const int32_t* __restrict__ xq,
+    int32_t* __restrict__ ctr, int nqb, int nkb, int64_t q_rows, int64_t q_valid,
+    int64_t kv_valid, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kB * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];
+  __shared__ int next_item;
+  const int home = xcc_id();
+  for (;;) {
+    if (threadIdx.x == 0) next_item = pop_item(items, xq, ctr, home);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(next_item);   // uniform: scalar loads below
+    __syncthreads();
+    if (item < 0) break;
+    attend_item(item, ks, vt, q, row_ptr, col_idx, col_slot, k, v, out, lse, nqb, nkb, q_rows,
+                q_valid, kv_valid, scale_log2);
+  }
+}
+
 template <int D, int BLK>
 hipError_t f32_launch(const Dims& g, const void* q, const int32_t* row_ptr,
                       const int32_t* col_idx, const int32_t* col_slot, const void* k,
@@ -413,20 +490,27 @@ hipError_t f32_launch(const Dims& g, const void* q, const int32_t* row_ptr,
 
 hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s) {
   const int rows = g.H * g.nqb;
-  int n2 = 1, idbits = 0;
-  while (n2 < rows) n2 <<= 1;
-  while ((1 << idbits) < rows) ++idbits;
-  int cbits = 0;
-  while ((1 << cbits) <= g.nkb) ++cbits;
-  if (n2 <= kQueueMax && idbits + cbits <= 31) {   // real keys stay below the sentinel
-    hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, s, row_ptr, rows, g.nkb,
-                       n2, idbits, items);
-  } else {
-    hipLaunchKernelGGL(identity_queue_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, rows,
-                       items);
-  }
+  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, s, row_ptr, rows, g.nkb, items,
+                     items + rows, items + rows + kXcd + 1);
   return hipGetLastError();
 }
+
+int queue_words(int rows) { return rows + 2 * kXcd + 1; }
+
+namespace {
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace
 
 bool attn_supported(int dtype, int d, int B) {
   if (dtype == SA_BF16) return d == kD && B == kB;
@@ -435,16 +519,17 @@ bool attn_supported(int dtype, int d, int B) {
 
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
-                       const void* v, void* out, float* lse, const int32_t* items,
+                       const void* v, void* out, float* lse, int32_t* items,
                        float sm_scale, hipStream_t s) {
   const int rows = g.H * g.nqb;
   if (g.dtype == SA_BF16) {
     if (g.d != kD || g.B != kB) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(rows), dim3(256), 0, s, (const uint16_t*)q,
+    const int grid = std::min(rows, 2 * cu_count());   // two resident workgroups per CU
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)q,
                        row_ptr, col_idx, col_slot, (const uint16_t*)k, (const uint16_t*)v,
-                       (uint16_t*)out, lse, items, g.nqb, g.nkb, g.q_rows, g.q_valid, g.kv_rows,
-                       g.kv_valid, scale_log2);
+                       (uint16_t*)out, lse, items, items + rows, items + rows + kXcd + 1, g.nqb,
+                       g.nkb, g.q_rows, g.q_valid, g.kv_valid, scale_log2);
     return hipGetLastError();
   }
   if (g.d == 64 && g.B == 64) return f32_launch<64, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, items, sm_scale, s);

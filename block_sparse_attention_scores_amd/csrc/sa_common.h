@@ -115,6 +115,6 @@ hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* 
 hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s);
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
-                       const void* v, void* out, float* lse, const int32_t* items,
+                       const void* v, void* out, float* lse, int32_t* items,
                        float sm_scale, hipStream_t s);
 }  // namespace sa
