@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_480p_32k.md")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc", "attn_fwd.hip")
 
 
@@ -56,11 +56,12 @@ def source_digest(path):
 
 
 def load_traffic(config_name, nnz):
-    """HBM bytes per attention launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
-    only if they were taken on the current kernel source and workload."""
+    """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, only if it was taken on the current kernel source and workload."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            line = next((l for l in f if l.startswith("traffic-record:")), None)
+        rec = json.loads(line.split(":", 1)[1]) if line else {}
     except (OSError, ValueError):
         return None
     r = rec.get(config_name)
