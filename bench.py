@@ -7,7 +7,9 @@ HBM: sparse_attn_select (pool, score, top-p/top-k, CSR) -> kv_demand_pack
 (demand union, packed gather) -> sparse_attn_forward (work queue, attention
 over the selected blocks).  Every stage is timed with HIP events on the
 stream the library launches on; L2 and the Infinity Cache are flushed
-(512 MiB write) before each step, outside the events.
+before each step, outside the events: a 512 MiB write evicts them, then a
+512 MiB read of another buffer forces the write-back of those dirty lines, so
+the first kernel of the step starts on cold, clean caches.
 
 Prints ONE JSON line.  ``value`` is selected-block attention TFLOP/s of the
 whole step, 4*B^2*d*nnz / step time; ``roofline`` is that of the dominant
@@ -127,7 +129,9 @@ def main():
     d = to_device(x, w)
     sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
     packed = not args.unpacked
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = None if args.no_flush else (
+        torch.empty(512 << 20, dtype=torch.uint8, device="cuda"),
+        torch.zeros(64 << 20, dtype=torch.int64, device="cuda"))
 
     def step(ev):
         ev[0].record()
@@ -157,7 +161,8 @@ def main():
     t0 = time.perf_counter()
     for k in range(args.steps):
         if flush is not None:
-            flush.fill_(k & 0xff)
+            flush[0].fill_(k & 0xff)
+            flush[1].amax()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

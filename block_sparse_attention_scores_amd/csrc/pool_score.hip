@@ -11,7 +11,7 @@
 // predictor the workgroup also projects its mean through W (fp64).
 //
 // score_kernel: S = scale * X Y^T per head in fp64 (X = pooled or projected
-// query blocks, Y = key blocks), 64x64 tiles staged through LDS.
+// query blocks, Y = key blocks) on the fp64 matrix cores.
 #include "sa_common.h"
 
 namespace sa {
@@ -70,18 +70,22 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
   const int n = (int)min((int64_t)BLK, valid - first);
 
   const int t = threadIdx.x, c = t % CPR, rl = t / CPR;
-  const T* base = x + ((int64_t)h * rows + first) * D + c * EPC;
+  // buffer descriptor over the block's valid rows only: rows at or past n read
+  // as 0 without a branch, so every load is issued up front
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(x + ((int64_t)h * rows + first) * D), (short)0,
+      (int)(n * D * (int)sizeof(T)), 0x00020000);
+  const int off = (rl * D + c * EPC) * (int)sizeof(T);
   uint4 v[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int r = rl + it * RL;
-    v[it] = (r < n) ? *reinterpret_cast<const uint4*>(base + (int64_t)r * D) : make_uint4(0, 0, 0, 0);
-  }
+  for (int it = 0; it < IT; ++it)
+    v[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, off, it * RL * D * (int)sizeof(T), 0));
   double acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int it = 0; it < IT; ++it) Elem<T>::add(acc, v[it]);  // padded loads are +0.0
+  for (int it = 0; it < IT; ++it) Elem<T>::add(acc, v[it]);  // rows past n read as +0.0
 #pragma unroll
   for (int e = 0; e < EPC; ++e) part[rl * D + c * EPC + e] = acc[e];
   __syncthreads();
@@ -106,52 +110,62 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
   }
 }
 
-// S[h, i, j] = scale * sum_c X[h, i, c] * Y[h, j, c]  (fp64, c ascending)
-constexpr int kTile = 64, kKc = 16;
+// S[h, i, j] = scale * sum_c X[h, i, c] * Y[h, j, c] in fp64 on the matrix
+// cores (v_mfma_f64_16x16x4_f64).  One wave per 16 x 16 output tile, four
+// tiles along j per workgroup.  The inner index (padded with zeros to 4*KPL)
+// is dealt to the four 16-lane groups in pairs: at steps 2c and 2c+1, lane
+// group g supplies indices 8c + 2g and 8c + 2g + 1 of its row of X (A operand,
+// row = lane % 16) and of its row of Y (B operand, column = lane % 16), so
+// each 16-byte load of a wave covers 64 contiguous bytes of 16 rows.  Output
+// element q of lane l is S[4*q + l/16][l % 16] of the tile.  Rows and columns
+// past the edge load 0 and are not stored.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+template <int KPL>  // steps per lane group: inner <= 4 * KPL
 __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ X,
                                                     const double* __restrict__ Y, int nx,
                                                     int ny, int inner, double scale,
                                                     double* __restrict__ S) {
-  __shared__ double xs[kTile][kKc + 1];
-  __shared__ double ys[kTile][kKc + 1];
-  const int h = blockIdx.z;
-  const int i0 = blockIdx.y * kTile, j0 = blockIdx.x * kTile;
-  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  const double* xh = X + (int64_t)h * nx * inner;
-  const double* yh = Y + (int64_t)h * ny * inner;
-  double acc[4][4] = {};
-  for (int c0 = 0; c0 < inner; c0 += kKc) {
-    for (int e = t; e < kTile * kKc; e += 256) {
-      const int r = e / kKc, cc = e % kKc;
-      const bool okc = c0 + cc < inner;
-      xs[r][cc] = (i0 + r < nx && okc) ? xh[(int64_t)(i0 + r) * inner + c0 + cc] : 0.0;
-      ys[r][cc] = (j0 + r < ny && okc) ? yh[(int64_t)(j0 + r) * inner + c0 + cc] : 0.0;
+  static_assert(KPL % 2 == 0, "pairs of doubles per load");
+  const int h = blockIdx.z, wv = threadIdx.x / kWave, l = lane_id();
+  const int i0 = blockIdx.y * 16, j0 = (blockIdx.x * 4 + wv) * 16;
+  if (j0 >= ny) return;  // whole wave; no barriers below
+  const int r = l % 16, g = l / 16;
+  const int xi = i0 + r, yj = j0 + r;
+  const double* xp = X + ((int64_t)h * nx + xi) * inner;
+  const double* yp = Y + ((int64_t)h * ny + yj) * inner;
+  f64x2 a[KPL / 2], b[KPL / 2];
+  if (inner == 4 * KPL) {  // no padding; rows are 16-byte aligned
+    const f64x2* xv = reinterpret_cast<const f64x2*>(xp);
+    const f64x2* yv = reinterpret_cast<const f64x2*>(yp);
+#pragma unroll
+    for (int s = 0; s < KPL / 2; ++s) {
+      a[s] = xi < nx ? xv[4 * s + g] : f64x2{0.0, 0.0};
+      b[s] = yj < ny ? yv[4 * s + g] : f64x2{0.0, 0.0};
     }
-    __syncthreads();
-    const int kc = min(kKc, inner - c0);
-    for (int cc = 0; cc < kc; ++cc) {
-      double a[4], b[4];
+  } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = xs[ty * 4 + u][cc];
-        b[u] = ys[tx * 4 + u][cc];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma(a[u], b[w], acc[u][w]);
+    for (int s = 0; s < KPL / 2; ++s) {
+      const int c0 = 8 * s + 2 * g, c1 = c0 + 1;
+      a[s].x = (xi < nx && c0 < inner) ? xp[c0] : 0.0;
+      a[s].y = (xi < nx && c1 < inner) ? xp[c1] : 0.0;
+      b[s].x = (yj < ny && c0 < inner) ? yp[c0] : 0.0;
+      b[s].y = (yj < ny && c1 < inner) ? yp[c1] : 0.0;
     }
-    __syncthreads();
   }
-  double* sh = S + (int64_t)h * nx * ny;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty * 4 + u;
-    if (i >= nx) continue;
+  for (int s = 0; s < KPL / 2; ++s) {
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].x, b[s].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].y, b[s].y, acc, 0, 0, 0);
+  }
+  const int j = j0 + r;
+  if (j < ny) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx * 4 + w;
-      if (j < ny) sh[(int64_t)i * ny + j] = scale * acc[u][w];
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + 4 * q + g;
+      if (i < nx) S[((int64_t)h * nx + i) * ny + j] = scale * acc[q];
     }
   }
 }
@@ -189,9 +203,20 @@ hipError_t launch_pool(const Dims& g, const void* q, const void* k, const float*
 
 hipError_t launch_scores(const Dims& g, const double* qx, const double* kx, int inner,
                          double scale, double* scores, hipStream_t s) {
-  dim3 grid((g.nkb + kTile - 1) / kTile, (g.nqb + kTile - 1) / kTile, g.H);
-  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale,
-                     scores);
+  const dim3 grid((g.nkb + 63) / 64, (g.nqb + 15) / 16, g.H);
+  if (inner <= 8) {
+    hipLaunchKernelGGL(score_kernel<2>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
+  } else if (inner <= 16) {
+    hipLaunchKernelGGL(score_kernel<4>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
+  } else if (inner <= 32) {
+    hipLaunchKernelGGL(score_kernel<8>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
+  } else if (inner <= 64) {
+    hipLaunchKernelGGL(score_kernel<16>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
+  } else if (inner <= 128) {
+    hipLaunchKernelGGL(score_kernel<32>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

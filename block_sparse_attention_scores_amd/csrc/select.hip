@@ -3,11 +3,17 @@
 // parallelism"; "Dynamic Sparsity in Large-Scale Video DiT Training", section
 // "The idea": rank the pairs and keep the critical ones).
 //
-// One workgroup per (head, query block) row.  The row's scores are staged in
-// LDS; top-p mode turns them into softmax masses (fp64, max-subtracted, sum in
-// a fixed order).  A bitonic sort in LDS orders (value descending, block id
-// ascending); the cumulative mass comes from a block-wide scan in fp64.  The
-// kept set is written as a bitmask row plus its count.
+// One single-wave workgroup per (head, query block) row.  Top-p mode turns
+// the row's scores into softmax masses (fp64, max-subtracted, sum in a fixed
+// order).  A bitonic sort orders (value descending, block id ascending); the
+// cumulative mass in that order comes from a wave scan in fp64.  The kept set
+// is written as a bitmask row plus its count.
+//
+// Rows of up to 1024 blocks are sorted in registers (select_reg_kernel: lane
+// l holds sorted positions l, l+64, ...; strides under 64 exchange across
+// lanes (DPP moves, or ds_bpermute for 16 and 32), larger ones swap
+// registers).  Longer rows go through LDS
+// (select_kernel).
 #include <float.h>
 
 #include "sa_common.h"
@@ -15,26 +21,24 @@
 namespace sa {
 namespace {
 
-constexpr int kSelThreads = 256;
-constexpr int kMaxKB = 4096;
-
 // a goes before b: larger value first, then lower block id
 __device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// LDS (dynamic): key[n2] fp64, idx[n2] int32, bits[W] uint32, n2 = pow2 >= nkb
+template <int kSelThreads>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const double* __restrict__ S, int nkb, int W, int mode, double top_p, int top_k,
+    const double* __restrict__ S, int nkb, int n2, int W, int mode, double top_p, int top_k,
     uint32_t* __restrict__ bits_out, int32_t* __restrict__ counts) {
-  __shared__ double key[kMaxKB];
-  __shared__ int idx[kMaxKB];
-  __shared__ uint32_t bits[kMaxKB / 32];
+  extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
+  double* key = reinterpret_cast<double*>(sel_lds);
+  int* idx = reinterpret_cast<int*>(key + n2);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(idx + n2);
   __shared__ double red[kSelThreads / kWave + 1];
   __shared__ int redi[kSelThreads / kWave + 1];
 
   const int row = blockIdx.x, t = threadIdx.x;
-  int n2 = 1;
-  while (n2 < nkb) n2 <<= 1;
   const double* s = S + (int64_t)row * nkb;
 
   if (mode == SA_TOP_P) {
@@ -124,12 +128,206 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (t == 0) counts[row] = c;
 }
 
+// Order-preserving map of an fp64 value onto uint64 (larger value, larger
+// key); -0.0 is folded onto +0.0 so that equal values compare equal.
+__device__ __forceinline__ uint64_t order_key(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & ~(1ull << 63)) : ~k;
+  return __longlong_as_double((long long)u);
+}
+// Value of lane (l ^ S) for S below 64.  Strides 1, 2 and 8 are a single DPP
+// move (quad_perm / row_ror:8); stride 4 picks between row_ror:4 and
+// row_ror:12 by lane bit 2; 16 and 32 go through ds_bpermute.
+template <int S>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (S == 4) {
+    const int a = __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true);
+    const int b = __builtin_amdgcn_mov_dpp(v, 0x12C, 0xF, 0xF, true);
+    return (threadIdx.x & 4) ? a : b;
+  } else if constexpr (S == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
+  } else {
+    return __shfl_xor(v, S, kWave);
+  }
+}
+template <int S>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
+  const int lo = xor_lane<S>((int)(uint32_t)v);
+  const int hi = xor_lane<S>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// a goes before b: larger key first, then lower block id
+__device__ __forceinline__ bool before_k(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// One compare-exchange stage of the bitonic network (block size SIZE, partner
+// distance STRIDE) over positions e = l + 64 k.
+template <int K, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&key)[K], int (&idx)[K], int l) {
+  if constexpr (STRIDE >= kWave) {
+    constexpr int ks = STRIDE / kWave;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k & ks) continue;
+      const int kb = k | ks;
+      const bool up = ((kWave * k) & SIZE) == 0;   // SIZE >= 128: lane bits do not matter
+      const bool sw = up ? before_k(key[kb], idx[kb], key[k], idx[k])
+                         : before_k(key[k], idx[k], key[kb], idx[kb]);
+      if (sw) {
+        const uint64_t tk = key[k]; key[k] = key[kb]; key[kb] = tk;
+        const int ti = idx[k]; idx[k] = idx[kb]; idx[kb] = ti;
+      }
+    }
+  } else {
+    const bool lower = (l & STRIDE) == 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint64_t pk = xor_lane<STRIDE>(key[k]);
+      const int pi = xor_lane<STRIDE>(idx[k]);
+      const bool up = ((l + kWave * k) & SIZE) == 0;
+      // the lower position of an ascending pair keeps the earlier element
+      const bool self_first = before_k(key[k], idx[k], pk, pi);
+      if (self_first != (lower == up)) { key[k] = pk; idx[k] = pi; }
+    }
+  }
+}
+
+// The whole network for 64 K elements: sizes 2, 4, ..., 64 K, each with
+// strides SIZE/2 down to 1.
+template <int K, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic(uint64_t (&key)[K], int (&idx)[K], int l) {
+  if constexpr (SIZE <= kWave * K) {
+    if constexpr (STRIDE == 0) {
+      bitonic<K, SIZE * 2, SIZE>(key, idx, l);
+    } else {
+      bitonic_stage<K, SIZE, STRIDE>(key, idx, l);
+      bitonic<K, SIZE, STRIDE / 2>(key, idx, l);
+    }
+  }
+}
+
+template <int K>  // elements per lane; the sort length is 64 * K
+__global__ __launch_bounds__(kWave) void select_reg_kernel(
+    const double* __restrict__ S, int nkb, int W, int mode, double top_p, int top_k,
+    uint32_t* __restrict__ bits_out, int32_t* __restrict__ counts) {
+  constexpr int N2 = kWave * K;
+  __shared__ uint32_t bits[N2 / 32];
+  const int row = blockIdx.x, l = threadIdx.x;
+  const double* s = S + (int64_t)row * nkb;
+
+  uint64_t key[K];
+  int idx[K];
+  if (mode == SA_TOP_P) {
+    double v[K];
+    double mx = -DBL_MAX;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = l + kWave * k;
+      v[k] = j < nkb ? s[j] : -DBL_MAX;
+      mx = fmax(mx, v[k]);
+    }
+    mx = wave_reduce(mx, [](double a, double b) { return fmax(a, b); });
+    double part = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = l + kWave * k;
+      v[k] = j < nkb ? exp(v[k] - mx) : 0.0;
+      part += v[k];
+    }
+    const double tot = wave_reduce(part, [](double a, double b) { return a + b; });
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = l + kWave * k;
+      key[k] = j < nkb ? order_key(v[k] / tot) : 0ull;   // padding sorts last
+      idx[k] = j < nkb ? j : 0x7fffffff;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = l + kWave * k;
+      key[k] = j < nkb ? order_key(s[j]) : 0ull;
+      idx[k] = j < nkb ? j : 0x7fffffff;
+    }
+  }
+  for (int w = l; w < N2 / 32; w += kWave) bits[w] = 0u;
+
+  // bitonic sort into "before" order over positions e = l + 64 k
+  bitonic<K, 2, 1>(key, idx, l);
+
+  const int kf = min(top_k, nkb);
+  int m;
+  if (mode == SA_TOP_P) {
+    if (top_p >= 1.0) {
+      m = nkb;
+    } else {
+      // cumulative mass in sorted order; count the positions still below p
+      double carry = 0.0;
+      int below = 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int e = l + kWave * k;
+        const double mass = e < nkb ? key_value(key[k]) : 0.0;
+        const double cs = carry + wave_inclusive_scan(mass);
+        below += __popcll(__ballot(e < nkb && cs < top_p));
+        carry = __shfl(cs, kWave - 1, kWave);
+      }
+      m = min(nkb, 1 + below);
+    }
+    m = max(m, kf);
+  } else {
+    m = kf;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int e = l + kWave * k, j = idx[k];
+    if (e < m && (unsigned)j < (unsigned)nkb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  int c = 0;
+  for (int w = l; w < W; w += kWave) {
+    bits_out[(int64_t)row * W + w] = bits[w];
+    c += __popc(bits[w]);
+  }
+  c = wave_reduce(c, [](int a, int b) { return a + b; });
+  if (l == 0) counts[row] = c;
+}
+
 }  // namespace
 
 hipError_t launch_select(const Dims& g, const double* scores, int mode, double top_p,
                          int top_k, uint32_t* bits, int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(g.H * g.nqb), dim3(kSelThreads), 0, s, scores, g.nkb,
-                     g.W, mode, top_p, top_k, bits, counts);
+  int n2 = 1;
+  while (n2 < g.nkb) n2 <<= 1;
+  const size_t lds = (size_t)n2 * (sizeof(double) + sizeof(int)) + (size_t)g.W * sizeof(uint32_t);
+  const dim3 grid(g.H * g.nqb);
+#define SA_SEL_REG(K)                                                                     \
+  hipLaunchKernelGGL(select_reg_kernel<K>, grid, dim3(kWave), 0, s, scores, g.nkb, g.W, mode, \
+                     top_p, top_k, bits, counts)
+  if (n2 <= 64) {
+    SA_SEL_REG(1);
+  } else if (n2 <= 128) {
+    SA_SEL_REG(2);
+  } else if (n2 <= 256) {
+    SA_SEL_REG(4);
+  } else if (n2 <= 512) {
+    SA_SEL_REG(8);
+  } else if (n2 <= 1024) {
+    SA_SEL_REG(16);
+  } else {
+    hipLaunchKernelGGL(select_kernel<256>, grid, dim3(256), lds, s, scores, g.nkb, n2, g.W,
+                       mode, top_p, top_k, bits, counts);
+  }
+#undef SA_SEL_REG
   return hipGetLastError();
 }
 
