@@ -78,13 +78,13 @@ SelectWs select_ws(const Dims& g) {
 }
 size_t csr_ws(const Dims& g) { return round_up(sizeof(int32_t) * g.H * g.nqb); }
 struct PackWs {
-  size_t bits, heads, total;
+  size_t part, slot_of, total;
 };
 PackWs pack_ws(const Dims& g) {
   PackWs w{};
   size_t o = 0;
-  w.bits = o; o += round_up(sizeof(uint32_t) * g.H * g.W);
-  w.heads = o; o += round_up(sizeof(int32_t) * g.H);
+  w.part = o; o += round_up(sizeof(uint32_t) * g.H * sa::mark_groups(g) * g.W);
+  w.slot_of = o; o += round_up(sizeof(int32_t) * g.H * g.nkb);
   w.total = o;
   return w;
 }
@@ -214,11 +214,11 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr, const int32_t
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PackWs w = pack_ws(g);
-  SA_TRY_HIP(sa::launch_demand(g, row_ptr, col_idx, at<uint32_t>(ws, w.bits),
-                               at<int32_t>(ws, w.heads), demand_ptr, demand_idx, col_slot,
-                               packed_cap_blocks, dev_status, s));
+  int32_t* slot_of = at<int32_t>(ws, w.slot_of);
+  SA_TRY_HIP(sa::launch_demand(g, row_ptr, col_idx, at<uint32_t>(ws, w.part), slot_of,
+                               demand_ptr, demand_idx, packed_cap_blocks, dev_status, s));
   SA_TRY_HIP(sa::launch_pack(g, demand_ptr, demand_idx, k, v, k_packed, v_packed,
-                             packed_cap_blocks, s));
+                             packed_cap_blocks, row_ptr, col_idx, slot_of, col_slot, s));
   return SA_OK;
 }
 

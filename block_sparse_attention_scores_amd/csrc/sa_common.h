@@ -105,13 +105,14 @@ hipError_t launch_count_bits(const Dims& g, const uint32_t* bits, int32_t* count
                              hipStream_t s);
 hipError_t launch_csr(const Dims& g, const uint32_t* bits, const int32_t* counts,
                       int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+int mark_groups(const Dims& g);
 hipError_t launch_demand(const Dims& g, const int32_t* row_ptr, const int32_t* col_idx,
-                         uint32_t* dem_bits, int32_t* head_count, int32_t* demand_ptr,
-                         int32_t* demand_idx, int32_t* col_slot, int64_t cap,
-                         int32_t* dev_status, hipStream_t s);
+                         uint32_t* part, int32_t* slot_of, int32_t* demand_ptr,
+                         int32_t* demand_idx, int64_t cap, int32_t* dev_status, hipStream_t s);
 hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* demand_idx,
                        const void* k, const void* v, void* kp, void* vp, int64_t cap,
-                       hipStream_t s);
+                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* slot_of,
+                       int32_t* col_slot, hipStream_t s);
 hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s);
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
