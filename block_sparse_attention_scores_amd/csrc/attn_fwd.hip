@@ -197,8 +197,6 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
 // bf16 MFMA path, d = 128, block = 128
 // ---------------------------------------------------------------------------
 constexpr int kD = 128, kB = 128;
-constexpr int kKsStride = kD + 8;   // K tile row stride in bf16 (272 B: 16-B reads conflict-free)
-constexpr int kVtStride = kB + 4;   // V^T tile row stride in bf16 (264 B = 66 dwords)
 constexpr int kTileBytes = kB * kD * 2;
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -222,84 +220,46 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int base) {
   return __builtin_convertvector(v, bf16x8);
 }
 
-// (a.lo, b.lo) and (a.hi, b.hi): 16-bit halves of two rows interleaved
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
+// K and V blocks go from global memory straight into LDS (buffer_load ... lds,
+// 16 bytes per lane, no staging registers).  One such load of a wave fills 1 KiB
+// of LDS, four 256-byte rows, lane L at byte 16 L; the lane chooses which
+// 16-byte chunk of its row it fetches, so each row is stored with its chunks
+// permuted (XOR swizzle) and the MFMA operand reads below hit 64 distinct banks:
+//   K: logical chunk c of row r sits at chunk c ^ (r & 15)
+//   V: logical chunk c of row r sits at chunk c ^ (4 (r & 3))
+// A block of 32 KiB is 32 such loads, 8 per wave.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 
-// Staging of one K/V block pair (global -> registers -> LDS).
-//  K: 16-byte chunk c16 = tid + 256*it (it < 8): row c16 >> 4, column chunk c16 & 15;
-//     global reads fully coalesced, LDS rows padded to 272 B.
-//  V: 4 keys x 8 d per thread and iteration (it < 2).  In a wave, lanes l give
-//     key group kg = (l & 15) + 16*(c & 1) and d chunk dc = (l >> 4) + 4*(c >> 1),
-//     c = wave + 4*it; 16 consecutive lanes hold 16 different key groups, so the
-//     transposed 8-byte writes V^T[d][4kg..4kg+3] of those lanes fall in 32
-//     distinct banks (row stride 66 dwords).
-struct Stage {
-  u32x4 k[8];
-  u32x4 v[2][4];
-};
-
-// The lane offsets below are recomputed from the thread id at every use (the
-// empty asm makes the id opaque, so it is not hoisted out of the loop): cheaper
-// than keeping them live across the loop, which spills at 256 registers.
-__device__ __forceinline__ int opaque_tid() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
-
-__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* kb, const uint16_t* vb,
-                                           int /*tid*/, int wave) {
-  const int tid = opaque_tid();
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, kTileBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, kTileBytes);
-  const int koff = (tid >> 4) * 256 + (tid & 15) * 16;
+__device__ __forceinline__ void dma_block(const uint16_t* src, uint16_t* lds, int wave,
+                                          const int (&voff)[4]) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, kTileBytes);
 #pragma unroll
-  for (int it = 0; it < 8; ++it) st.k[it] = buf_load16(rk, koff, it * 4096);
-  const int l = tid & 63;
-  const int voff = (4 * (l & 15)) * 256 + (l >> 4) * 16;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int c = wave + 4 * it;
-    const int base = (64 * (c & 1)) * 256 + (4 * (c >> 1)) * 16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.v[it][r] = buf_load16(rv, voff, base + r * 256);
+  for (int ii = 0; ii < 8; ++ii) {
+    const int i = 8 * wave + ii;   // rows 4i .. 4i+3
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + i * 512), 16, voff[ii & 3],
+                                             i * 1024, 0, 0);
   }
 }
 
-__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* ks, uint16_t* vt,
-                                            int /*tid*/, int wave) {
-  const int tid = opaque_tid();
-#pragma unroll
-  for (int it = 0; it < 8; ++it)
-    *reinterpret_cast<u32x4*>(ks + ((tid >> 4) + 16 * it) * kKsStride + (tid & 15) * 8) = st.k[it];
-  const int l = tid & 63;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int c = wave + 4 * it;
-    const int kg = (l & 15) + 16 * (c & 1);
-    const int dc = (l >> 4) + 4 * (c >> 1);
-    uint16_t* dst = vt + (8 * dc) * kVtStride + 4 * kg;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      u32x2 lo, hi;   // d = 8dc + 2cc (low halves) and 8dc + 2cc + 1 (high halves)
-      lo.x = pack_lo(st.v[it][0][cc], st.v[it][1][cc]);
-      lo.y = pack_lo(st.v[it][2][cc], st.v[it][3][cc]);
-      hi.x = pack_hi(st.v[it][0][cc], st.v[it][1][cc]);
-      hi.y = pack_hi(st.v[it][2][cc], st.v[it][3][cc]);
-      *reinterpret_cast<u32x2*>(dst + (2 * cc) * kVtStride) = lo;
-      *reinterpret_cast<u32x2*>(dst + (2 * cc + 1) * kVtStride) = hi;
-    }
-  }
+// 8 bytes at LDS byte address `addr`, transposed within 16-lane groups
+// (ds_read_b64_tr_b16): element e of lane j is element j%4 of what lane
+// 4e + j/4 of the group addressed.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* base, int addr) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)(lds_void*)base + addr));
+  return __builtin_bit_cast(u32x2, v);
 }
 
-// One (head, query block) item by one workgroup of four waves.
+// One (head, query block) item by one workgroup of four waves.  Per key block:
+//   S phase      S^T = K Q^T on MFMA (K from LDS, Q in registers)
+//   barrier      (all waves done with K; this wave's V loads have landed)
+//   K loads      the next block's K goes into LDS
+//   softmax, PV  O^T += V^T P^T (V from LDS through transposing reads)
+//   barrier      (all waves done with V; the next K has landed)
+//   V loads      the next block's V goes into LDS
 __device__ __forceinline__ void attend_item(
-    int item, uint16_t* ks, uint16_t* vt, const uint16_t* __restrict__ q,
+    int item, uint16_t* kl, uint16_t* vl, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ col_slot, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -309,6 +269,30 @@ __device__ __forceinline__ void attend_item(
   const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
   const int h = item / nqb, i = item % nqb;
   const int qloc = 32 * wave + lq;                                // query row within the block
+
+  // lane offsets of the block loads (see dma_block): row 4i + L/16, chunk L%16
+  int kvo[4], vvo[4];
+  {
+    const int rr = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      kvo[p] = rr * 256 + ((pc ^ (4 * p + rr)) << 4);
+      vvo[p] = rr * 256 + ((pc ^ (4 * rr)) << 4);
+    }
+  }
+  // K operand reads: row 32t + lq, logical chunk 2s + g -> chunk (2s + g) ^ (lq & 15)
+  int ka[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ka[s] = lq * 256 + (((2 * s + g) ^ (lq & 15)) << 4);
+  // V operand reads (transposing): lane j of 16-lane group a reads row
+  // 4 kga + e, columns 32u + 16 (a & 1) + 4 q .. +3, with e = j / 4, q = j % 4
+  int va[4];
+  {
+    const int a = lane >> 4, j = lane & 15, e = j >> 2, qq = j & 3;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      va[u] = 1024 * g + 256 * e + 64 * (u ^ e) + 32 * (a & 1) + 8 * qq;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): d = 16s + 8g .. +8
   bf16x8 qf[8];
@@ -338,36 +322,40 @@ __device__ __forceinline__ void attend_item(
     return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(col_slot[e]) : (int64_t)h * nkb + j;
   };
 
-  Stage st;
   int e = e0;
   int64_t blk = -1;
   while (e < e1 && (blk = block_of(e)) < 0) ++e;
-  if (e < e1) stage_load(st, k + blk * (kB * kD), v + blk * (kB * kD), tid, wave);
+  if (e < e1) {
+    dma_block(k + blk * (kB * kD), kl, wave, kvo);
+    dma_block(v + blk * (kB * kD), vl, wave, vvo);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   while (e < e1) {
     const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
-    __syncthreads();                 // all waves are done reading the previous tiles
-    stage_store(st, ks, vt, tid, wave);
-    __syncthreads();
-    // prefetch the next block while this one is computed
     int en = e + 1;
     int64_t bn = -1;
     while (en < e1 && (bn = block_of(en)) < 0) ++en;
-    if (en < e1) stage_load(st, k + bn * (kB * kD), v + bn * (kB * kD), tid, wave);
 
     // S^T tile t: keys 32t.., this lane's query; reg r -> key 32t + 8(r/4) + 4g + r%4
     f32x16 sacc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + (32 * t + lq) * kKsStride + 16 * s + 8 * g);
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            reinterpret_cast<const char*>(kl) + ka[s] + t * 8192);
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
       }
-    }
+
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
+    __syncthreads();
+    if (en < e1) dma_block(k + bn * (kB * kD), kl, wave, kvo);
 
     // valid keys of this block (uniform); only the sequence's last block is ragged
     const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
@@ -400,8 +388,9 @@ __device__ __forceinline__ void attend_item(
 
     // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
     // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
-    // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g.  The exp of tile t+1
-    // is independent of the MFMAs of tile t, so the two can overlap.
+    // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g (the transposing reads
+    // at rows 4 kga + e and 4 (kga + 2) + e).  The exp of tile t+1 is
+    // independent of the MFMAs of tile t, so the two can overlap.
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -414,19 +403,22 @@ __device__ __forceinline__ void attend_item(
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
-        const int kga = 8 * t + 4 * h2 + g;
+        const int rows = 1024 * (8 * t + 4 * h2);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint16_t* vrow = vt + (32 * u + lq) * kVtStride;
-          const u32x2 va = *reinterpret_cast<const u32x2*>(vrow + 4 * kga);
-          const u32x2 vb2 = *reinterpret_cast<const u32x2*>(vrow + 4 * (kga + 2));
-          const u32x4 vw = {va.x, va.y, vb2.x, vb2.y};
+          const u32x2 lo = lds_read_tr(vl, va[u] + rows);
+          const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
+          const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
           oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
                                                             oacc[u], 0, 0, 0);
         }
       }
     }
     l_run += ps;
+
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's K loads of the next block
+    __syncthreads();
+    if (en < e1) dma_block(v + bn * (kB * kD), vl, wave, vvo);
     e = en;
   }
 
@@ -459,8 +451,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     float* __restrict__ lse, const int32_t* __restrict__ items, const int32_t* __restrict__ xq,
     int32_t* __restrict__ ctr, int nqb, int nkb, int64_t q_rows, int64_t q_valid,
     int64_t kv_valid, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kB * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kVtStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t kl[kB * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl[kB * kD];
   __shared__ int next_item;
   const int home = xcc_id();
   for (;;) {
@@ -469,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const int item = __builtin_amdgcn_readfirstlane(next_item);   // uniform: scalar loads below
     __syncthreads();
     if (item < 0) break;
-    attend_item(item, ks, vt, q, row_ptr, col_idx, col_slot, k, v, out, lse, nqb, nkb, q_rows,
+    attend_item(item, kl, vl, q, row_ptr, col_idx, col_slot, k, v, out, lse, nqb, nkb, q_rows,
                 q_valid, kv_valid, scale_log2);
   }
 }
