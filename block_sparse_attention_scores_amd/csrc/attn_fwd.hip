@@ -344,6 +344,9 @@ __device__ __forceinline__ void attend_item(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+    // Raised wave priority for the score MFMAs: the other workgroup's wave on
+    // this SIMD, usually in its softmax, fills the issue slots these leave.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
@@ -353,6 +356,7 @@ __device__ __forceinline__ void attend_item(
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
       }
 
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
     __syncthreads();
     if (en < e1) dma_block(k + bn * (kB * kD), kl, wave, kvo);
@@ -373,18 +377,22 @@ __device__ __forceinline__ void attend_item(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-    const float mn = fmaxf(m_run, mx);
-    // v_exp_f32 directly: masses below 2^-126 flush to 0, which softmax tolerates
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-    // rescale O only if some query's running max moved (wave-uniform branch)
-    if (__ballot(m_run != mn)) {
+    // The running max only moves when some query's block max exceeds it by
+    // more than 8 (log2 units): until then P = exp2(S*scale - m) stays below
+    // 2^8, and softmax does not depend on which reference max is used.  Most
+    // rescales of O are skipped (wave-uniform branch).
+    if (__ballot(mx > m_run + 8.f)) {
+      const float mn = fmaxf(m_run, mx);
+      // v_exp_f32 directly: masses below 2^-126 flush to 0, which softmax tolerates
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
+      l_run *= alpha;
+      m_run = mn;
     }
-    l_run *= alpha;
-    m_run = mn;
+    const float mn = m_run;
 
     // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
     // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
