@@ -344,6 +344,49 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Video-aware block organisation (token order in 3-D tiles)
+# ---------------------------------------------------------------------------
+def video_block_order(latent: Sequence[int], tile: Sequence[int]) -> np.ndarray:
+    """Top-p abstract (mlsift listing): the frontend organises video tokens
+    into blocks in a video-aware way.  The pages give no layout; the reading
+    here: the tokens of the (T, Hl, Wl) latent, raster order, are reordered
+    so that consecutive positions fill 3-D tiles of shape (tt, th, tw) - tiles
+    taken in raster order over the tile grid, tokens in raster order inside a
+    tile, tiles at the far edges clipped to the latent.  Blocks are then runs
+    of B consecutive positions, as in the raster layout.  Returns `order`
+    with order[p] = raster index of the token at position p (int64)."""
+    T, Hl, Wl = latent
+    tt, th, tw = tile
+    t, y, x = np.indices((T, Hl, Wl)).reshape(3, -1)
+    ny, nx = -(-Hl // th), -(-Wl // tw)
+    tile_id = ((t // tt) * ny + y // th) * nx + x // tw
+    inside = ((t % tt) * th + y % th) * tw + x % tw
+    return np.lexsort((inside, tile_id)).astype(np.int64)
+
+
+def query_block_order(order: np.ndarray, q_start: int, q_valid: int) -> np.ndarray:
+    """A query share (raster tokens q_start .. q_start+q_valid-1) keeps its
+    tokens and takes them in the order they appear in `order`.  Returns
+    query-local row indices (int64)."""
+    sel = (order >= q_start) & (order < q_start + q_valid)
+    return order[sel] - q_start
+
+
+def inverse_order(order: np.ndarray) -> np.ndarray:
+    inv = np.empty_like(order)
+    inv[order] = np.arange(len(order), dtype=order.dtype)
+    return inv
+
+
+def permute_rows(x: np.ndarray, idx: np.ndarray, rows_out: int) -> np.ndarray:
+    """out[h, r] = x[h, idx[r]] for r < len(idx); rows after that are zero
+    (the padding the path expects)."""
+    out = np.zeros((x.shape[0], rows_out) + x.shape[2:], dtype=x.dtype)
+    out[:, :len(idx)] = x[:, idx]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # diagnostic only: exact block mass (the full-scores approach)
 # ---------------------------------------------------------------------------
 def exact_block_mass(q: np.ndarray, k: np.ndarray, q_valid: int, kv_valid: int,

@@ -495,3 +495,94 @@ def test_padded_keys_never_attended():
     k2[:, 20:] = 1e3; v2[:, 20:] = -1e3
     o2, _ = O.attention(q, k2, v2, m, 16, 20, B, 0.3)
     np.testing.assert_array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# video-aware block organisation
+# ---------------------------------------------------------------------------
+def _tile_order_by_loops(latent, tile):
+    """Independent construction: walk the tile grid, then each tile's box."""
+    T, Hl, Wl = latent
+    tt, th, tw = tile
+    out = []
+    for a in range(0, T, tt):
+        for b in range(0, Hl, th):
+            for c in range(0, Wl, tw):
+                for t in range(a, min(a + tt, T)):
+                    for y in range(b, min(b + th, Hl)):
+                        for x in range(c, min(c + tw, Wl)):
+                            out.append((t * Hl + y) * Wl + x)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("latent,tile", [((3, 5, 7), (2, 2, 3)), ((4, 8, 8), (2, 4, 4)),
+                                         ((5, 9, 11), (2, 8, 8)), ((1, 3, 17), (1, 2, 5)),
+                                         ((21, 30, 52), (2, 8, 8))])
+def test_video_order_matches_loop_construction(latent, tile):
+    o = O.video_block_order(latent, tile)
+    np.testing.assert_array_equal(o, _tile_order_by_loops(latent, tile))
+    assert np.array_equal(np.sort(o), np.arange(int(np.prod(latent))))
+
+
+@pytest.mark.parametrize("latent", [(3, 5, 7), (2, 6, 4)])
+def test_video_order_identity_cases(latent):
+    n = int(np.prod(latent))
+    for tile in [(1, 1, 1), tuple(latent), (1, latent[1], latent[2]), (2, latent[1], latent[2])]:
+        np.testing.assert_array_equal(O.video_block_order(latent, tile), np.arange(n))
+
+
+def test_video_order_divisible_runs_are_tile_boxes():
+    latent, tile = (4, 8, 16), (2, 4, 4)
+    o = O.video_block_order(latent, tile)
+    t, y, x = np.unravel_index(o, latent)
+    run = 2 * 4 * 4
+    for p0 in range(0, len(o), run):
+        sl = slice(p0, p0 + run)
+        for c, ext in zip((t, y, x), tile):
+            v = c[sl]
+            assert v.max() - v.min() == ext - 1 and v.min() % ext == 0
+
+
+def test_video_order_makes_cluster_pure_blocks():
+    """Blocks of 2x8x8 tiles nest inside the generator's 4x8x8 cluster tiles:
+    every block of 128 positions then carries one cluster id, while raster
+    blocks of a frame row mix several."""
+    w = I.Workload("tile_pin", heads=1, head_dim=64, block=128, dtype="f32", latent=(4, 16, 32),
+                   q_start=0, q_valid=4 * 16 * 32, seed=3, strength=1.0, tile=(4, 8, 8),
+                   clusters=16)
+    cid = I.token_cluster_ids(w)
+    o = O.video_block_order(w.latent, (2, 8, 8))
+    tiled = cid[o].reshape(-1, 128)
+    assert all(len(set(r)) == 1 for r in tiled)
+    raster = cid.reshape(-1, 128)
+    assert any(len(set(r)) > 1 for r in raster)
+
+
+def test_query_order_and_inverse():
+    latent, tile = (5, 9, 11), (2, 4, 4)
+    o = O.video_block_order(latent, tile)
+    n = len(o)
+    np.testing.assert_array_equal(O.query_block_order(o, 0, n), o)
+    inv = O.inverse_order(o)
+    np.testing.assert_array_equal(o[inv], np.arange(n))
+    np.testing.assert_array_equal(inv[o], np.arange(n))
+    q0, qn = 37, 200
+    qo = O.query_block_order(o, q0, qn)
+    assert np.array_equal(np.sort(qo), np.arange(qn))
+    pos = inv[qo + q0]                                 # positions in the full order
+    assert np.all(np.diff(pos) > 0)                    # same relative order as `order`
+    # a share that is whole frames keeps the same token set, in tile order
+    frame = latent[1] * latent[2]
+    qo2 = O.query_block_order(o, 0, 2 * frame)
+    np.testing.assert_array_equal(qo2, o[:2 * frame])
+
+
+def test_permute_rows_roundtrip_and_padding():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 50, 3)).astype(np.float32)
+    o = rng.permutation(50)
+    y = O.permute_rows(x, o, 64)
+    assert np.all(y[:, 50:] == 0)
+    np.testing.assert_array_equal(y[:, :50], x[:, o])
+    back = O.permute_rows(y, O.inverse_order(o), 50)
+    np.testing.assert_array_equal(back, x)
