@@ -29,7 +29,8 @@ SA_SCORE_POOLED, SA_SCORE_LOWRANK = 0, 1
 SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-           "kv_demand_pack", "sparse_attn_forward", "sa_status_string", "sa_abi_version")
+           "kv_demand_pack", "sparse_attn_forward", "sa_video_block_order", "sa_permute_rows",
+           "sa_status_string", "sa_abi_version")
 
 
 class SaProblem(ctypes.Structure):
@@ -50,6 +51,11 @@ class SaProblem(ctypes.Structure):
         ("score_mode", ctypes.c_int32),
         ("rank", ctypes.c_int32),
     ]
+
+
+class SaVideoTiling(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("frames", "height", "width", "tile_t", "tile_h", "tile_w")]
 
 
 class SparseAttnError(RuntimeError):
@@ -80,11 +86,14 @@ def load(path: str = None):
     lib.sparse_attn_csr_from_mask.argtypes = [prob, P, P, P, P, sz, P]
     lib.kv_demand_pack.argtypes = [prob, P, P, P, P, P, P, P, P, P, i64, P, P, sz, P]
     lib.sparse_attn_forward.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.sa_video_block_order.argtypes = [ctypes.POINTER(SaVideoTiling), i64, i64, P, P, P, P, P]
+    lib.sa_permute_rows.argtypes = [i32, i64, i32, P, P, i64, P, i64, P]
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_abi_version.argtypes = []
     for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-                 "kv_demand_pack", "sparse_attn_forward", "sa_abi_version"):
+                 "kv_demand_pack", "sparse_attn_forward", "sa_video_block_order",
+                 "sa_permute_rows", "sa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -154,6 +163,23 @@ def sparse_attn_forward(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, 
     _check("sparse_attn_forward", load().sparse_attn_forward(
         ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
         _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def video_tiling(latent, tile) -> SaVideoTiling:
+    return SaVideoTiling(*[int(v) for v in tuple(latent) + tuple(tile)])
+
+
+def sa_video_block_order(tiling, q_start, q_valid, kv_order, kv_inverse, q_order, q_inverse,
+                         stream=None):
+    _check("sa_video_block_order", load().sa_video_block_order(
+        ctypes.byref(tiling), int(q_start), int(q_valid), _ptr(kv_order), _ptr(kv_inverse),
+        _ptr(q_order), _ptr(q_inverse), _stream(stream)))
+
+
+def sa_permute_rows(heads, rows, row_bytes, idx, src, src_rows, dst, dst_rows, stream=None):
+    _check("sa_permute_rows", load().sa_permute_rows(
+        int(heads), int(rows), int(row_bytes), _ptr(idx), _ptr(src), int(src_rows), _ptr(dst),
+        int(dst_rows), _stream(stream)))
 
 
 def default_scale(d: int) -> float:

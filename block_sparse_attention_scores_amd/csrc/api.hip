@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -122,7 +124,7 @@ T* at(void* ws, size_t off) {
 
 extern "C" {
 
-int sa_abi_version(void) { return 1; }
+int sa_abi_version(void) { return 2; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -242,6 +244,41 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
   SA_TRY_HIP(sa::launch_queue(g, row_ptr, items, s));
   SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, items,
                              sm, s));
+  return SA_OK;
+}
+
+int sa_video_block_order(const sa_video_tiling* tiling, int64_t q_start, int64_t q_valid,
+                         int32_t* kv_order, int32_t* kv_inverse, int32_t* q_order,
+                         int32_t* q_inverse, void* stream) {
+  if (!tiling || !kv_order || !kv_inverse || !q_order || !q_inverse) return SA_ERR_INVALID_ARG;
+  const sa_video_tiling& t = *tiling;
+  if (t.frames < 1 || t.height < 1 || t.width < 1) return SA_ERR_INVALID_ARG;
+  if (t.tile_t < 1 || t.tile_h < 1 || t.tile_w < 1) return SA_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)t.frames * t.height * t.width;
+  if (n >= ((int64_t)1 << 31)) return SA_ERR_UNSUPPORTED;
+  if (q_start < 0 || q_valid < 1 || q_start + q_valid > n) return SA_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)kv_order, (const void*)kv_inverse, (const void*)q_order,
+                        (const void*)q_inverse})
+    if ((uintptr_t)p & 3u) return SA_ERR_INVALID_ARG;
+  SA_TRY_HIP(sa::launch_video_order(t.frames, t.height, t.width, t.tile_t, t.tile_h, t.tile_w,
+                                    q_start, q_valid, kv_order, kv_inverse, q_order, q_inverse,
+                                    static_cast<hipStream_t>(stream)));
+  return SA_OK;
+}
+
+int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_t* idx,
+                    const void* src, int64_t src_rows, void* dst, int64_t dst_rows,
+                    void* stream) {
+  if (heads < 1 || rows < 0 || src_rows < 0 || dst_rows < rows) return SA_ERR_INVALID_ARG;
+  if (row_bytes < 4 || row_bytes > 65536 || row_bytes % 4) return SA_ERR_INVALID_ARG;
+  if (!dst || (rows > 0 && (!idx || !src))) return SA_ERR_INVALID_ARG;
+  if (((uintptr_t)dst & 3u) || ((uintptr_t)src & 3u) || ((uintptr_t)idx & 3u))
+    return SA_ERR_INVALID_ARG;
+  if ((int64_t)heads * std::max(src_rows, dst_rows) >= ((int64_t)1 << 40)) return SA_ERR_UNSUPPORTED;
+  if (dst_rows == 0) return SA_OK;
+  const bool wide = row_bytes % 16 == 0 && aligned16(src) && aligned16(dst);
+  SA_TRY_HIP(sa::launch_permute_rows(heads, rows, row_bytes, idx, src, src_rows, dst, dst_rows,
+                                     wide, static_cast<hipStream_t>(stream)));
   return SA_OK;
 }
 

@@ -118,4 +118,10 @@ hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
                        const void* v, void* out, float* lse, int32_t* items,
                        float sm_scale, hipStream_t s);
+hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int64_t q_start,
+                              int64_t q_valid, int32_t* order, int32_t* inverse, int32_t* q_order,
+                              int32_t* q_inverse, hipStream_t s);
+hipError_t launch_permute_rows(int heads, int64_t rows, int row_bytes, const int32_t* idx,
+                               const void* src, int64_t src_rows, void* dst, int64_t dst_rows,
+                               bool wide, hipStream_t s);
 }  // namespace sa

@@ -118,3 +118,40 @@ def to_device(x: dict, w: Workload, device="cuda"):
         out["wq"] = torch.from_numpy(x["wq"]).to(device).contiguous()
         out["wk"] = torch.from_numpy(x["wk"]).to(device).contiguous()
     return out
+
+
+class VideoLayout:
+    """Token orders of one latent in 3-D tile order (sa_video_block_order),
+    and the row gathers that move Q, K, V into that order and O, LSE back
+    (sa_permute_rows).  The orders are computed on the device once per shape.
+
+    latent: (T, Hl, Wl) of the key/value sequence; tile: (tt, th, tw);
+    the query share is raster tokens q_start .. q_start + q_valid - 1."""
+
+    def __init__(self, latent, tile, q_start: int, q_valid: int, device="cuda"):
+        n = int(latent[0]) * int(latent[1]) * int(latent[2])
+        i32 = dict(dtype=torch.int32, device=device)
+        self.latent, self.tile = tuple(latent), tuple(tile)
+        self.kv_order = torch.empty(n, **i32)
+        self.kv_inverse = torch.empty(n, **i32)
+        self.q_order = torch.empty(q_valid, **i32)
+        self.q_inverse = torch.empty(q_valid, **i32)
+        B.sa_video_block_order(B.video_tiling(latent, tile), q_start, q_valid, self.kv_order,
+                               self.kv_inverse, self.q_order, self.q_inverse)
+
+    @staticmethod
+    def gather(x, idx, rows_out: int, out=None):
+        """out[h, r] = x[h, idx[r]] for r < len(idx), zero after (x: [H, rows, ...])."""
+        H, rows_in = x.shape[0], x.shape[1]
+        row_bytes = x[0, 0].numel() * x.element_size()
+        if out is None:
+            out = torch.empty((H, rows_out) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+        B.sa_permute_rows(H, idx.numel(), row_bytes, idx, x, rows_in, out, rows_out)
+        return out
+
+    def to_tiles(self, q, k, v, q_rows: int, kv_rows: int):
+        return (self.gather(q, self.q_order, q_rows), self.gather(k, self.kv_order, kv_rows),
+                self.gather(v, self.kv_order, kv_rows))
+
+    def to_raster(self, x, rows_out: int, out=None):
+        return self.gather(x, self.q_inverse, rows_out, out)

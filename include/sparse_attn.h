@@ -171,10 +171,53 @@ int sparse_attn_forward(const sa_problem* prob, const void* q,
                         const void* v_src, void* out, float* lse_opt, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ---- video-aware block organisation --------------------------------------
+ * The Top-p sparse-attention abstract (mlsift listing, tag "sequence
+ * parallelism") organises video tokens into blocks in a video-aware way; the
+ * page gives no layout.  Reading implemented here: the tokens of a
+ * (frames, height, width) latent, raster order, are reordered so consecutive
+ * positions fill 3-D tiles of (tile_t, tile_h, tile_w) tokens: tiles in
+ * raster order over the tile grid, tokens in raster order inside a tile,
+ * tiles at the far edges clipped to the latent.  The path then runs on the
+ * reordered rows unchanged (blocks are runs of B consecutive positions); with
+ * tile_t*tile_h*tile_w == B and dimensions divisible by the tile, every block
+ * is one tile. */
+typedef struct sa_video_tiling {   /* host struct, read synchronously */
+  int32_t frames, height, width;   /* latent (T, Hl, Wl), each >= 1 */
+  int32_t tile_t, tile_h, tile_w;  /* tile shape, each >= 1 */
+} sa_video_tiling;
+
+/* The orders of one latent and one query share (raster tokens q_start ..
+ * q_start + q_valid - 1, 0 <= q_start, 1 <= q_valid, q_start + q_valid <= N,
+ * N = frames * height * width < 2^31):
+ *   kv_order[p]   = raster index of the token at position p        int32 [N]
+ *   kv_inverse[r] = position of raster token r                     int32 [N]
+ *   q_order[p]    = query-local raster row (0 .. q_valid-1) of the p-th
+ *                   query token in kv_order                        int32 [q_valid]
+ *   q_inverse[r]  = position in q_order of query-local row r       int32 [q_valid]
+ * The query share keeps its tokens and takes them in the order they appear
+ * in kv_order.  Computed on the device once per shape; no workspace. */
+int sa_video_block_order(const sa_video_tiling* tiling, int64_t q_start, int64_t q_valid,
+                         int32_t* kv_order, int32_t* kv_inverse, int32_t* q_order,
+                         int32_t* q_inverse, void* stream);
+
+/* Row gather for every head: dst[h, r] = src[h, idx[r]] for r < rows, and
+ * dst[h, r] = 0 for rows <= r < dst_rows (the zero padding the path needs).
+ * Rows are row_bytes bytes (a multiple of 4, at most 65536); src is
+ * [heads, src_rows, row_bytes], dst [heads, dst_rows, row_bytes].  An index
+ * outside [0, src_rows) yields a zero row.  With kv_order / q_order this puts
+ * Q, K, V into the tiled layout; with q_inverse it brings O (row_bytes =
+ * d * element size) and the LSE (row_bytes = 4) back to raster order.  src
+ * and dst must not overlap; 16-byte aligned pointers and rows take the wide
+ * path. */
+int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_t* idx,
+                    const void* src, int64_t src_rows, void* dst, int64_t dst_rows,
+                    void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 plus the video block order entry points). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

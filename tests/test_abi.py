@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 1
+    assert lib.sa_abi_version() == 2
 
 
 def test_struct_layout_matches_c():
@@ -151,3 +151,38 @@ def test_csr_argument_errors(lib):
     assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE * 4, 0, None) == B.SA_ERR_WORKSPACE
     assert f(None, FAKE, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
+
+
+FAKE = 0x10000   # never dereferenced: every case below fails validation first
+
+
+def test_video_order_validation(lib):
+    f = B.load().sa_video_block_order
+    good = B.video_tiling((21, 30, 52), (2, 8, 8))
+    n = 21 * 30 * 52
+    assert f(None, 0, n, FAKE, FAKE, FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(B.video_tiling((21, 30, 52), (0, 8, 8))), 0, n, FAKE, FAKE, FAKE, FAKE,
+             None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(B.video_tiling((0, 30, 52), (2, 8, 8))), 0, n, FAKE, FAKE, FAKE, FAKE,
+             None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(good), 1, n, FAKE, FAKE, FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(good), 0, 0, FAKE, FAKE, FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(good), 0, n, FAKE, None, FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(good), 0, n, FAKE + 2, FAKE, FAKE, FAKE, None) == B.SA_ERR_INVALID_ARG
+    big = B.video_tiling((2048, 1024, 1024), (2, 8, 8))
+    assert f(ctypes.byref(big), 0, 1, FAKE, FAKE, FAKE, FAKE, None) == B.SA_ERR_UNSUPPORTED
+
+
+def test_permute_rows_validation(lib):
+    f = B.load().sa_permute_rows
+    assert f(0, 10, 256, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG   # heads
+    assert f(2, 10, 6, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG     # row bytes
+    assert f(2, 10, 0, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
+    assert f(2, 10, 65540, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
+    assert f(2, 20, 256, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG   # rows > dst
+    assert f(2, 10, 256, None, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG   # no idx
+    assert f(2, 10, 256, FAKE, None, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG   # no src
+    assert f(2, 10, 256, FAKE, FAKE, 10, None, 16, None) == B.SA_ERR_INVALID_ARG   # no dst
+    assert f(2, 10, 256, FAKE, FAKE + 2, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
+    assert f(2, -1, 256, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
+    assert f(2, 0, 256, None, None, 0, FAKE, 0, None) == B.SA_OK                   # nothing to do
