@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-items", type=int, default=256,
                     help="(head, query block) items in the oracle's timed sample")
+    ap.add_argument("--tiles", default=None, metavar="TT,TH,TW",
+                    help="video-aware block organisation: Q, K, V are gathered into 3-D tile "
+                         "order before select and O, LSE back to raster order after forward "
+                         "(both inside the timed step)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device copy of MIB MiB (untimed), the "
                          "known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counters")
@@ -118,7 +122,7 @@ def main():
     import numpy as np
     import torch
     from block_sparse_attention_scores_amd import binding, inputs as I
-    from block_sparse_attention_scores_amd.path import SparseAttention, to_device
+    from block_sparse_attention_scores_amd.path import SparseAttention, VideoLayout, to_device
 
     binding.load()                       # fails loudly if the HIP library is missing
     if not torch.cuda.is_available():
@@ -127,7 +131,15 @@ def main():
     w = I.named(args.config)
     x = I.generate(w)
     d = to_device(x, w)
-    sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
+    tiles = tuple(int(v) for v in args.tiles.split(",")) if args.tiles else None
+    if tiles:
+        lay = VideoLayout(w.latent, tiles, w.q_start, w.q_valid)
+        qt, kt, vt = (torch.empty_like(d[n]) for n in ("q", "k", "v"))
+        out_r = torch.empty_like(d["q"])
+        lse_r = torch.empty(w.heads, w.q_rows, 1, dtype=torch.float32, device="cuda")
+        sa = SparseAttention(w, qt, kt, vt, d.get("wq"), d.get("wk"))
+    else:
+        sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
     packed = not args.unpacked
     flush = None if args.no_flush else (
         torch.empty(512 << 20, dtype=torch.uint8, device="cuda"),
@@ -135,13 +147,22 @@ def main():
 
     def step(ev):
         ev[0].record()
-        sa.select()
+        if tiles:
+            lay.gather(d["q"], lay.q_order, w.q_rows, out=qt)
+            lay.gather(d["k"], lay.kv_order, w.kv_rows, out=kt)
+            lay.gather(d["v"], lay.kv_order, w.kv_rows, out=vt)
         ev[1].record()
+        sa.select()
+        ev[2].record()
         if packed:
             sa.pack()
-        ev[2].record()
-        sa.forward(packed=packed)
         ev[3].record()
+        sa.forward(packed=packed)
+        ev[4].record()
+        if tiles:
+            lay.to_raster(sa.out, w.q_rows, out=out_r)
+            lay.to_raster(sa.lse.unsqueeze(-1), w.q_rows, out=lse_r)
+        ev[5].record()
 
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
@@ -151,7 +172,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -167,10 +188,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    sel = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    pck = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    fwd = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    tot = sel + pck + fwd
+    pin = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    sel = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    pck = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    fwd = np.array([e[3].elapsed_time(e[4]) for e in evs])
+    pout = np.array([e[4].elapsed_time(e[5]) for e in evs])
+    tot = pin + sel + pck + fwd + pout
     nnz = sa.nnz()
     dense_pairs = w.heads * w.n_qb * w.n_kb
     flops = 4.0 * w.block * w.block * w.head_dim * nnz
@@ -198,10 +221,13 @@ def main():
                    "latent_thw": list(w.latent), "top_p": w.top_p, "top_k": w.top_k,
                    "select_mode": "top_p" if w.select_mode == 0 else "top_k",
                    "score": "pooled" if w.score_mode == 0 else f"lowrank{w.rank}",
-                   "packed_kv": packed, "cache": "warm" if flush is None else "flushed each step"},
+                   "packed_kv": packed, "cache": "warm" if flush is None else "flushed each step",
+                   "layout": "tiles " + "x".join(map(str, tiles)) if tiles else "raster"},
         "ms_per_layer": round(ms_step, 4),
         "stages_ms": {"select": round(float(sel.mean()), 4), "pack": round(float(pck.mean()), 4),
                       "forward": round(fwd_ms, 4),
+                      **({"permute_in": round(float(pin.mean()), 4),
+                          "permute_out": round(float(pout.mean()), 4)} if tiles else {}),
                       "forward_p10_p90": [round(float(np.percentile(fwd, 10)), 4),
                                           round(float(np.percentile(fwd, 90)), 4)]},
         "selected_blocks": nnz, "dense_blocks": dense_pairs,

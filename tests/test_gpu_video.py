@@ -114,3 +114,62 @@ def test_path_in_tile_order(latent, tile, extra):
     assert np.array_equal(lse_r.cpu().numpy(), want_l)
     say(f"  selected {mask.mean():.3f} (raster layout selects "
         f"{O.select(O.scores_for(x['q'], x['k'], w.q_valid, w.kv_valid, w.block, w.score_mode, w.eff_score_scale)[2], w.select_mode, w.top_p, w.top_k)[0].mean():.3f}), excused {exc}")
+
+
+@pytest.mark.parametrize("name", ["480p", "720p_rank"])
+def test_full_size_tile_order(name):
+    """The benchmark's tile-order leg at full size: selection, CSR and demand
+    on every row, attention on sampled items, O and LSE back in raster order;
+    prints the selected fraction and the recall of the true attention mass on
+    the sampled rows for both layouts."""
+    from test_gpu_fullsize import sampled_items
+    w = I.named(name)
+    tile = (2, 8, 8)
+    say("tile order", w.name, tile)
+    x = I.generate(w)
+    o = O.video_block_order(w.latent, tile)
+    qo = O.query_block_order(o, w.q_start, w.q_valid)
+    xt = dict(x)
+    xt["q"] = O.permute_rows(x["q"][:, :w.q_valid], qo, w.q_rows)
+    xt["k"] = O.permute_rows(x["k"][:, :w.kv_valid], o, w.kv_rows)
+    xt["v"] = O.permute_rows(x["v"][:, :w.kv_valid], o, w.kv_rows)
+
+    d = to_device(x, w)
+    lay = VideoLayout(w.latent, tile, w.q_start, w.q_valid)
+    qt, kt, vt = lay.to_tiles(d["q"], d["k"], d["v"], w.q_rows, w.kv_rows)
+    del d
+    sa = SparseAttention(w, qt, kt, vt, keep_means=True)
+    sa.run(packed=True)
+    out_r = lay.to_raster(sa.out, w.q_rows)
+    torch.cuda.synchronize()
+    assert int(sa.dev_status.item()) == 0
+    mask, excused = check_selection(w, sa, xt)
+    rp, ci = sa.host_csr()
+    orp, oci = O.csr(mask)
+    np.testing.assert_array_equal(rp, orp)
+    np.testing.assert_array_equal(ci, oci)
+    dp, di, _, cs = O.demand(mask, orp, oci)
+    np.testing.assert_array_equal(sa.demand_ptr.cpu().numpy(), dp)
+    np.testing.assert_array_equal(sa.col_slot[:orp[-1]].cpu().numpy(), cs)
+
+    items = sampled_items(w, orp, n_random=3)
+    check_attention(w, sa, mask, xt, items=items)
+    # raster output = gather of the tiled output (rows of the sampled items)
+    inv = torch.from_numpy(O.inverse_order(qo)).long()
+    go_t = sa.out[:, :w.q_valid].cpu()
+    assert torch.equal(out_r[:, :w.q_valid].cpu(), go_t[:, inv])
+
+    # selected fraction and recall of the true block mass, both layouts
+    _, _, s_r = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
+                             w.eff_score_scale)
+    mask_r, _ = O.select(s_r, w.select_mode, w.top_p, w.top_k)
+    rec = {}
+    for tag, xx, mm in (("raster", x, mask_r), ("tiles", xt, mask)):
+        vals = [float((O.exact_block_mass(xx["q"], xx["k"], w.q_valid, w.kv_valid, w.block,
+                                          w.eff_sm_scale, h, i) * mm[h, i]).sum())
+                for h, i in items]
+        rec[tag] = (mm.mean(), float(np.mean(vals)), float(np.min(vals)))
+    for tag, (frac, mean_r, min_r) in rec.items():
+        say(f"  {tag:6s}: selected fraction {frac:.4f}, recall of true mass on {len(items)} "
+            f"sampled rows mean {mean_r:.4f} min {min_r:.4f}")
+    say(f"  near-tie rows excused (tiles): {excused}")
