@@ -344,6 +344,53 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Backward of the attention under a block mask (the training workload)
+# ---------------------------------------------------------------------------
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
+                       q_valid: int, kv_valid: int, block: int, sm_scale: float,
+                       dout: np.ndarray, dtype=np.float64):
+    """Gradients of `attention` (same mask, same padding rules) for an
+    upstream gradient dO.  The DSV explainer's speedups are training numbers
+    ("What it costs"), so the sparse attention is differentiated: with
+    z = sm_scale <q_a, k_b> over the selected keys and P = softmax(z),
+        dV = P^T dO,   dP = dO V^T,   D_a = <dO_a, O_a>,
+        dS = P * (dP - D),   dQ = sm_scale dS K,   dK = sm_scale dS^T Q.
+    O is this oracle's own forward.  Padded query rows and rows with nothing
+    selected contribute nothing; keys at or past kv_valid get zero gradient.
+    Computed per (head, query block) in ``dtype``; returns dQ, dK, dV shaped
+    like q, k, v."""
+    H, q_rows, d = q.shape
+    nqb = q_rows // block
+    dq = np.zeros(q.shape, dtype)
+    dk = np.zeros(k.shape, dtype)
+    dv = np.zeros(v.shape, dtype)
+    key_ok = np.arange(k.shape[1]) < kv_valid
+    for h in range(H):
+        kh, vh = k[h].astype(dtype), v[h].astype(dtype)
+        for i in range(nqb):
+            lo, hi = i * block, min((i + 1) * block, q_valid)
+            if hi <= lo:
+                continue
+            allowed = np.repeat(mask[h, i], block) & key_ok
+            if not allowed.any():
+                continue
+            qc = q[h, lo:hi].astype(dtype)
+            go = dout[h, lo:hi].astype(dtype)
+            z = np.matmul(qc, kh.T) * dtype(sm_scale)
+            z[:, ~allowed] = -np.inf
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            o = np.matmul(p, vh)
+            dp = np.matmul(go, vh.T)
+            dd = (go * o).sum(axis=1, keepdims=True)
+            ds = p * (dp - dd)
+            dq[h, lo:hi] = dtype(sm_scale) * np.matmul(ds, kh)
+            dk[h] += dtype(sm_scale) * np.matmul(ds.T, qc)
+            dv[h] += np.matmul(p.T, go)
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
 # Video-aware block organisation (token order in 3-D tiles)
 # ---------------------------------------------------------------------------
 def video_block_order(latent: Sequence[int], tile: Sequence[int]) -> np.ndarray:

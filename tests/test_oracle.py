@@ -586,3 +586,72 @@ def test_permute_rows_roundtrip_and_padding():
     np.testing.assert_array_equal(y[:, :50], x[:, o])
     back = O.permute_rows(y, O.inverse_order(o), 50)
     np.testing.assert_array_equal(back, x)
+
+
+# ---------------------------------------------------------------------------
+# attention backward
+# ---------------------------------------------------------------------------
+def _autograd_grads(q, k, v, allowed_rows, allowed, dout, scale):
+    """torch autograd in fp64 over dense masked attention of the given rows."""
+    qt = torch.tensor(q[allowed_rows], dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    z = (qt @ kt.T) * scale
+    z = z.masked_fill(~torch.from_numpy(allowed[allowed_rows]), float("-inf"))
+    o = torch.softmax(z, dim=1) @ vt
+    o.backward(torch.tensor(dout[allowed_rows], dtype=torch.float64))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_backward_is_autograd_with_block_mask_and_padding():
+    H, B, d = 2, 16, 32
+    qv, kv = 64 - 5, 96 - 11
+    q, k, v = _qkv(31, H, 64, 96, d)
+    q[:, qv:] = 0; k[:, kv:] = 0; v[:, kv:] = 0
+    dout = np.random.default_rng(32).standard_normal((H, 64, d)).astype(np.float32)
+    mask = _random_mask(33, H=H, nqb=4, nkb=6, density=0.5)
+    mask[0, 1, :] = False
+    dq, dk, dv = O.attention_backward(q, k, v, mask, qv, kv, B, 0.2, dout)
+    for h in range(H):
+        allowed = np.repeat(np.repeat(mask[h], B, axis=0), B, axis=1)
+        allowed[:, kv:] = False
+        rows = [a for a in range(qv) if allowed[a].any()]
+        gq, gk, gv = _autograd_grads(q[h], k[h], v[h], rows, allowed, dout[h], 0.2)
+        np.testing.assert_allclose(dq[h][rows], gq, atol=1e-10, rtol=1e-9)
+        np.testing.assert_allclose(dk[h], gk, atol=1e-10, rtol=1e-9)
+        np.testing.assert_allclose(dv[h], gv, atol=1e-10, rtol=1e-9)
+        other = [a for a in range(64) if a not in rows]
+        assert np.all(dq[h][other] == 0)
+        assert np.all(dk[h][kv:] == 0) and np.all(dv[h][kv:] == 0)
+
+
+def test_backward_finite_differences_fp64():
+    H, B, d = 1, 4, 3
+    q, k, v = _qkv(34, H, 8, 12, d)
+    q = q.astype(np.float64); k = k.astype(np.float64); v = v.astype(np.float64)
+    mask = np.array([[[True, False, True], [False, True, True]]])
+    dout = np.random.default_rng(35).standard_normal((H, 8, d))
+    dq, dk, dv = O.attention_backward(q, k, v, mask, 8, 11, B, 0.6, dout)
+
+    def loss(qq, kk, vv):
+        o, _ = O.attention(qq, kk, vv, mask, 8, 11, B, 0.6, dtype=np.float64)
+        return float((o * dout).sum())
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 1, 2), (0, 5, 0), (0, x.shape[1] - 3, 1), (0, x.shape[1] - 1, 2)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps; xm[idx] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7, (name, idx, fd, g[idx])
+
+
+def test_backward_key_gradients_sum_to_zero():
+    """Each row's dS sums to zero over its keys, so dK summed over keys is 0."""
+    H, B, d = 2, 16, 8
+    q, k, v = _qkv(36, H, 48, 64, d)
+    dout = np.random.default_rng(37).standard_normal((H, 48, d)).astype(np.float32)
+    mask = _random_mask(38, H=H, nqb=3, nkb=4, density=0.6)
+    _, dk, _ = O.attention_backward(q, k, v, mask, 48, 64, B, 0.3, dout)
+    np.testing.assert_allclose(dk.sum(axis=1), 0, atol=1e-12)
