@@ -26,11 +26,11 @@ SA_ERR_CAPACITY = -5
 SA_F32, SA_BF16 = 0, 1
 SA_TOP_P, SA_TOP_K = 0, 1
 SA_SCORE_POOLED, SA_SCORE_LOWRANK = 0, 1
-SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD = 0, 1, 2, 3
+SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD, SA_STAGE_BACKWARD = 0, 1, 2, 3, 4
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-           "kv_demand_pack", "sparse_attn_forward", "sa_video_block_order", "sa_permute_rows",
-           "sa_status_string", "sa_abi_version")
+           "kv_demand_pack", "sparse_attn_forward", "sparse_attn_backward",
+           "sa_video_block_order", "sa_permute_rows", "sa_status_string", "sa_abi_version")
 
 
 class SaProblem(ctypes.Structure):
@@ -86,14 +86,15 @@ def load(path: str = None):
     lib.sparse_attn_csr_from_mask.argtypes = [prob, P, P, P, P, sz, P]
     lib.kv_demand_pack.argtypes = [prob, P, P, P, P, P, P, P, P, P, i64, P, P, sz, P]
     lib.sparse_attn_forward.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.sparse_attn_backward.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.sa_video_block_order.argtypes = [ctypes.POINTER(SaVideoTiling), i64, i64, P, P, P, P, P]
     lib.sa_permute_rows.argtypes = [i32, i64, i32, P, P, i64, P, i64, P]
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_abi_version.argtypes = []
     for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-                 "kv_demand_pack", "sparse_attn_forward", "sa_video_block_order",
-                 "sa_permute_rows", "sa_abi_version"):
+                 "kv_demand_pack", "sparse_attn_forward", "sparse_attn_backward",
+                 "sa_video_block_order", "sa_permute_rows", "sa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -163,6 +164,14 @@ def sparse_attn_forward(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, 
     _check("sparse_attn_forward", load().sparse_attn_forward(
         ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
         _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_backward(prob, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv, ws,
+                         ws_bytes, stream=None):
+    _check("sparse_attn_backward", load().sparse_attn_backward(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(row_ptr), _ptr(col_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes,
+        _stream(stream)))
 
 
 def video_tiling(latent, tile) -> SaVideoTiling:

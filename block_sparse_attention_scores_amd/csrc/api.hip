@@ -91,6 +91,19 @@ PackWs pack_ws(const Dims& g) {
   return w;
 }
 size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * sa::queue_words(g.H * g.nqb)); }
+struct BackwardWs {
+  size_t delta, counts, col_ptr, row_idx, total;
+};
+BackwardWs backward_ws(const Dims& g) {
+  BackwardWs w{};
+  size_t o = 0;
+  w.delta = o; o += round_up(sizeof(float) * g.H * g.q_rows);
+  w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nkb);
+  w.col_ptr = o; o += round_up(sizeof(int32_t) * (g.H * g.nkb + 1));
+  w.row_idx = o; o += round_up(sizeof(int32_t) * (size_t)g.H * g.nqb * g.nkb);
+  w.total = o;
+  return w;
+}
 
 size_t stage_bytes(const Dims& g, int stage) {
   switch (stage) {
@@ -98,6 +111,7 @@ size_t stage_bytes(const Dims& g, int stage) {
     case SA_STAGE_CSR: return csr_ws(g);
     case SA_STAGE_PACK: return pack_ws(g).total;
     case SA_STAGE_FORWARD: return forward_ws(g);
+    case SA_STAGE_BACKWARD: return backward_ws(g).total;
   }
   return 0;
 }
@@ -124,7 +138,7 @@ T* at(void* ws, size_t off) {
 
 extern "C" {
 
-int sa_abi_version(void) { return 2; }
+int sa_abi_version(void) { return 3; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -143,7 +157,7 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes) {
   if (!bytes) return SA_ERR_INVALID_ARG;
   const int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  if (stage < SA_STAGE_SELECT || stage > SA_STAGE_FORWARD) return SA_ERR_INVALID_ARG;
+  if (stage < SA_STAGE_SELECT || stage > SA_STAGE_BACKWARD) return SA_ERR_INVALID_ARG;
   *bytes = stage_bytes(g, stage);
   return SA_OK;
 }
@@ -244,6 +258,30 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
   SA_TRY_HIP(sa::launch_queue(g, row_ptr, items, s));
   SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, items,
                              sm, s));
+  return SA_OK;
+}
+
+int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
+                         void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (g.dtype != SA_BF16 || !sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out || !dout || !lse || !row_ptr || !col_idx || !dq || !dk || !dv)
+    return SA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return SA_ERR_INVALID_ARG;
+  if ((uintptr_t)lse & 15u) return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_BACKWARD, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  const BackwardWs w = backward_ws(g);
+  const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
+  SA_TRY_HIP(sa::launch_backward(g, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv,
+                                 at<float>(ws, w.delta), at<int32_t>(ws, w.counts),
+                                 at<int32_t>(ws, w.col_ptr), at<int32_t>(ws, w.row_idx), sm,
+                                 static_cast<hipStream_t>(stream)));
   return SA_OK;
 }
 

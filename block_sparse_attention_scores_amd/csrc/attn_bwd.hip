@@ -1,0 +1,383 @@
+// Backward of the block-sparse attention (the training workload: the DSV
+// explainer's speedups, "What it costs", are training numbers).  For the
+// forward's P = softmax(z), z = sm_scale <q_a, k_b> over the selected blocks:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = sm_scale dS K,  dK = sm_scale dS^T Q.
+// P is recomputed from the forward's LSE, never stored.
+//
+//   delta_kernel    D per query row (fp32), one wave per row
+//   csc_*_kernel    the transpose of the CSR block lists (per key block, the
+//                   query blocks that selected it, ascending): count, scan, fill
+//   bwd_dq_kernel   one workgroup per (head, query block): over its CSR row,
+//                   S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//   bwd_dkdv_kernel one workgroup per (head, key block): over its CSC column,
+//                   S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
+// All GEMMs are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
+// rounded to bf16 as MFMA operands.  Blocks arrive in LDS through direct loads
+// with the K swizzle (logical 16-byte chunk c of row r at c ^ (r & 15)); the
+// same rows are read either as MFMA A rows (ds_read_b128) or transposed
+// (ds_read_b64_tr_b16).
+#include <math.h>
+
+#include <algorithm>
+
+#include "mfma_bf16.h"
+
+namespace sa {
+namespace {
+
+using namespace bf16mma;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out,
+                                                    const uint16_t* __restrict__ dout,
+                                                    int64_t rows_total, int64_t q_rows,
+                                                    int64_t q_valid, float* __restrict__ delta) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows_total) return;   // whole wave
+  float s = 0.f;
+  if (row % q_rows < q_valid) {
+    const uint32_t o2 = reinterpret_cast<const uint32_t*>(out + row * kD)[lane];
+    const uint32_t d2 = reinterpret_cast<const uint32_t*>(dout + row * kD)[lane];
+    s = fmaf(bf16_lo(o2), bf16_lo(d2), bf16_hi(o2) * bf16_hi(d2));
+  }
+  s = wave_reduce(s, [](float a, float b) { return a + b; });
+  if (lane == 0) delta[row] = s;
+}
+
+// is key block j in CSR row [e0, e1) (ascending, unique ids)?
+__device__ __forceinline__ bool in_row(const int32_t* __restrict__ col_idx, int e0, int e1, int j) {
+  while (e0 < e1) {
+    const int m = (e0 + e1) >> 1;
+    const int c = col_idx[m];
+    if (c == j) return true;
+    if (c < j) e0 = m + 1; else e1 = m;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(256) void csc_count_kernel(const int32_t* __restrict__ row_ptr,
+                                                        const int32_t* __restrict__ col_idx, int H,
+                                                        int nqb, int nkb, int32_t* __restrict__ counts) {
+  for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < H * nkb; u += gridDim.x * blockDim.x) {
+    const int h = u / nkb, j = u % nkb;
+    int c = 0;
+    for (int i = 0; i < nqb; ++i) {
+      const int r = h * nqb + i;
+      c += in_row(col_idx, row_ptr[r], row_ptr[r + 1], j) ? 1 : 0;
+    }
+    counts[u] = c;
+  }
+}
+
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void csc_scan_kernel(const int32_t* __restrict__ counts,
+                                                                int n, int32_t* __restrict__ col_ptr) {
+  __shared__ int scratch[kScanThreads / kWave + 1];
+  int base = 0;
+  for (int p0 = 0; p0 < n; p0 += kScanThreads) {
+    const int p = p0 + threadIdx.x;
+    const int c = p < n ? counts[p] : 0;
+    int total;
+    const int incl = block_inclusive_scan(c, scratch, &total);
+    if (p < n) col_ptr[p] = base + incl - c;
+    base += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) col_ptr[n] = base;
+}
+
+__global__ __launch_bounds__(256) void csc_fill_kernel(const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx, int H,
+                                                       int nqb, int nkb,
+                                                       const int32_t* __restrict__ col_ptr,
+                                                       int32_t* __restrict__ row_idx) {
+  for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < H * nkb; u += gridDim.x * blockDim.x) {
+    const int h = u / nkb, j = u % nkb;
+    int o = col_ptr[u];
+    for (int i = 0; i < nqb; ++i) {
+      const int r = h * nqb + i;
+      if (in_row(col_idx, row_ptr[r], row_ptr[r + 1], j)) row_idx[o++] = i;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// lane-constant LDS offsets of one wave (K swizzle throughout)
+struct Offsets {
+  int dma[4];    // direct loads: row 4i + L/16, physical chunk L%16
+  int rowa[8];   // A rows: row lq (+32t via immediate), logical chunk 2s + g
+  int tr[4][2];  // transposed A: rows 4 kgb + e (kgb & 3 = g, g+2), columns 32u + 16(a&1) + 4q
+};
+
+__device__ __forceinline__ void make_offsets(Offsets& o, int lane) {
+  const int lq = lane & 31, g = lane >> 5;
+  const int rr = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) o.dma[p] = rr * 256 + ((pc ^ (4 * p + rr)) << 4);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o.rowa[s] = lq * 256 + (((2 * s + g) ^ (lq & 15)) << 4);
+  const int a = lane >> 4, jj = lane & 15, e = jj >> 2, qq = jj & 3;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kg = g + 2 * hh;              // low two bits of the row group
+      const int c16 = 4 * u + 2 * (a & 1) + (qq >> 1);
+      o.tr[u][hh] = 1024 * kg + 256 * e + ((c16 ^ (4 * kg + e)) << 4) + 8 * (qq & 1);
+    }
+}
+
+// A operand rows 32t + lq of a swizzled tile, k-step s
+__device__ __forceinline__ bf16x8 rows_a(const uint16_t* tile, const Offsets& o, int t, int s) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + o.rowa[s] +
+                                          t * 8192);
+}
+// transposed A operand, columns 32u.. of the tile, rows of k-step (t, h2)
+__device__ __forceinline__ bf16x8 cols_a(const uint16_t* tile, const Offsets& o, int u, int t,
+                                         int h2) {
+  const int rows = 1024 * (8 * t + 4 * h2);
+  const u32x2 lo = lds_read_tr(tile, o.tr[u][0] + rows);
+  const u32x2 hi = lds_read_tr(tile, o.tr[u][1] + rows);
+  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// fragments of row `row` of a [rows, 128] bf16 tensor as the B operand:
+// k-step s holds columns 16s + 8g .. +8
+__device__ __forceinline__ void load_b(bf16x8 (&f)[8], const uint16_t* base, int64_t row,
+                                       int64_t rows, int g) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)(rows * kD * 2));
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    f[s] = __builtin_bit_cast(bf16x8, buf_load16(r, (int)(row * 256) + 16 * g, 32 * s));
+}
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    uint16_t* __restrict__ dq, int nqb, int nkb, int64_t q_rows, int64_t q_valid,
+    int64_t kv_rows, int64_t kv_valid, float scale_log2, float sm_scale) {
+  __shared__ __attribute__((aligned(1024))) uint16_t kl[kB * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl[kB * kD];
+  const int item = blockIdx.x;
+  const int h = item / nqb, i = item % nqb;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
+  Offsets off;
+  make_offsets(off, lane);
+  const int64_t qrow = (int64_t)i * kB + 32 * wave + lq;   // this lane's query
+  const int64_t qbase = (int64_t)h * q_rows;
+
+  bf16x8 qf[8], df[8];
+  load_b(qf, q + qbase * kD, qrow, q_rows, g);
+  load_b(df, dout + qbase * kD, qrow, q_rows, g);
+  const float l = lse[qbase + qrow];
+  const bool live = qrow < q_valid && l > -INFINITY;
+  const float lse2 = live ? l * kLog2e : INFINITY;   // +inf: P = 0
+  const float dlt = delta[qbase + qrow];
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+
+  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[item]);
+  const int e1 = __builtin_amdgcn_readfirstlane(row_ptr[item + 1]);
+  for (int e = e0; e < e1; ++e) {
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
+    if ((unsigned)j >= (unsigned)nkb) continue;
+    const int64_t src = ((int64_t)h * kv_rows + (int64_t)j * kB) * kD;
+    __syncthreads();   // previous block's tiles are no longer read
+    dma_block(k + src, kl, wave, off.dma);
+    dma_block(v + src, vl, wave, off.dma);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dpacc[r] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(kl, off, t, s), qf[s], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(vl, off, t, s), df[s], dpacc, 0, 0, 0);
+      }
+      // reg r: key 32t + 8(r/4) + 4g + r%4 of this lane's query
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float p = key < lim ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
+        ds[r] = p * (dpacc[r] - dlt);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 dsf = to_bf16x8(ds, 8 * h2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(kl, off, u, t, h2), dsf, acc[u],
+                                                           0, 0, 0);
+      }
+    }
+  }
+  // dQ[query][d], reg r of tile u -> d = 32u + 8(r/4) + 4g + r%4
+  uint16_t* op = dq + (qbase + qrow) * kD;
+  const float sc = qrow < q_valid ? sm_scale : 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 o4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o4[x] = acc[u][4 * r4 + x] * sc;
+      *reinterpret_cast<bf16x4*>(op + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(o4, bf16x4);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int nqb, int nkb, int64_t q_rows,
+    int64_t q_valid, int64_t kv_rows, int64_t kv_valid, float scale_log2, float sm_scale) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ql[kB * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t dl[kB * kD];
+  __shared__ __attribute__((aligned(16))) float lse_s[kB];
+  __shared__ __attribute__((aligned(16))) float dlt_s[kB];
+  const int unit = blockIdx.x;
+  const int h = unit / nkb, j = unit % nkb;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
+  Offsets off;
+  make_offsets(off, lane);
+  const int64_t krow = (int64_t)j * kB + 32 * wave + lq;   // this lane's key
+  const int64_t kbase = (int64_t)h * kv_rows;
+  const bool key_ok = krow < kv_valid;
+
+  bf16x8 kf[8], vf[8];
+  load_b(kf, k + kbase * kD, krow, kv_rows, g);
+  load_b(vf, v + kbase * kD, krow, kv_rows, g);
+
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dka[u][r] = 0.f; dva[u][r] = 0.f; }
+
+  const int c0 = __builtin_amdgcn_readfirstlane(col_ptr[unit]);
+  const int c1 = __builtin_amdgcn_readfirstlane(col_ptr[unit + 1]);
+  for (int c = c0; c < c1; ++c) {
+    const int i = __builtin_amdgcn_readfirstlane(row_idx[c]);
+    const int64_t qb = (int64_t)h * q_rows + (int64_t)i * kB;
+    __syncthreads();   // previous query block's tiles are no longer read
+    dma_block(q + qb * kD, ql, wave, off.dma);
+    dma_block(dout + qb * kD, dl, wave, off.dma);
+    if (tid < kB) {
+      const int64_t row = (int64_t)i * kB + tid;
+      const float l = lse[qb + tid];
+      lse_s[tid] = (row < q_valid && l > -INFINITY) ? l * kLog2e : INFINITY;   // +inf: P = 0
+      dlt_s[tid] = delta[qb + tid];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dpacc[r] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(ql, off, t, s), kf[s], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(dl, off, t, s), vf[s], dpacc, 0, 0, 0);
+      }
+      // reg r: query 32t + 8(r/4) + 4g + r%4 against this lane's key
+      f32x16 p, ds;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int q0 = 32 * t + 8 * r4 + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + q0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_s + q0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * r4 + x;
+          const float pv =
+              key_ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l4[x])) : 0.f;
+          p[r] = pv;
+          ds[r] = pv * (dpacc[r] - d4[x]);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 pf = to_bf16x8(p, 8 * h2);
+        const bf16x8 dsf = to_bf16x8(ds, 8 * h2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(dl, off, u, t, h2), pf, dva[u],
+                                                           0, 0, 0);
+          dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(ql, off, u, t, h2), dsf, dka[u],
+                                                           0, 0, 0);
+        }
+      }
+    }
+  }
+  // dK, dV [key][d], reg r of tile u -> d = 32u + 8(r/4) + 4g + r%4
+  uint16_t* kp = dk + (kbase + krow) * kD;
+  uint16_t* vp = dv + (kbase + krow) * kD;
+  const float sk = key_ok ? sm_scale : 0.f, sv = key_ok ? 1.f : 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 k4, v4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        k4[x] = dka[u][4 * r4 + x] * sk;
+        v4[x] = dva[u][4 * r4 + x] * sv;
+      }
+      *reinterpret_cast<bf16x4*>(kp + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(k4, bf16x4);
+      *reinterpret_cast<bf16x4*>(vp + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Dims& g, const void* q, const void* k, const void* v,
+                           const void* out, const void* dout, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
+                           void* dv, float* delta, int32_t* counts, int32_t* col_ptr,
+                           int32_t* row_idx, float sm_scale, hipStream_t s) {
+  const int64_t qrows_total = (int64_t)g.H * g.q_rows;
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((qrows_total + 3) / 4)), dim3(256), 0, s,
+                     (const uint16_t*)out, (const uint16_t*)dout, qrows_total, g.q_rows,
+                     g.q_valid, delta);
+  const int cols = g.H * g.nkb;
+  const int grid = std::min((cols + 255) / 256, 1024);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(grid), dim3(256), 0, s, row_ptr, col_idx, g.H, g.nqb,
+                     g.nkb, counts);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, cols, col_ptr);
+  hipLaunchKernelGGL(csc_fill_kernel, dim3(grid), dim3(256), 0, s, row_ptr, col_idx, g.H, g.nqb,
+                     g.nkb, col_ptr, row_idx);
+  const float scale_log2 = sm_scale * kLog2e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(g.H * g.nqb), dim3(256), 0, s, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, delta,
+                     row_ptr, col_idx, (uint16_t*)dq, g.nqb, g.nkb, g.q_rows, g.q_valid,
+                     g.kv_rows, g.kv_valid, scale_log2, sm_scale);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(cols), dim3(256), 0, s, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, delta,
+                     col_ptr, row_idx, (uint16_t*)dk, (uint16_t*)dv, g.nqb, g.nkb, g.q_rows,
+                     g.q_valid, g.kv_rows, g.kv_valid, scale_log2, sm_scale);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -124,4 +124,9 @@ hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int
 hipError_t launch_permute_rows(int heads, int64_t rows, int row_bytes, const int32_t* idx,
                                const void* src, int64_t src_rows, void* dst, int64_t dst_rows,
                                bool wide, hipStream_t s);
+hipError_t launch_backward(const Dims& g, const void* q, const void* k, const void* v,
+                           const void* out, const void* dout, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
+                           void* dv, float* delta, int32_t* counts, int32_t* col_ptr,
+                           int32_t* row_idx, float sm_scale, hipStream_t s);
 }  // namespace sa

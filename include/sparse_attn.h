@@ -62,7 +62,8 @@ typedef enum sa_stage {
   SA_STAGE_SELECT = 0,   /* sparse_attn_select         */
   SA_STAGE_CSR = 1,      /* sparse_attn_csr_from_mask  */
   SA_STAGE_PACK = 2,     /* kv_demand_pack             */
-  SA_STAGE_FORWARD = 3   /* sparse_attn_forward        */
+  SA_STAGE_FORWARD = 3,  /* sparse_attn_forward        */
+  SA_STAGE_BACKWARD = 4  /* sparse_attn_backward       */
 } sa_stage;
 
 /* Problem description (host struct, read during the call only).
@@ -171,6 +172,28 @@ int sparse_attn_forward(const sa_problem* prob, const void* q,
                         const void* v_src, void* out, float* lse_opt, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Gradients of sparse_attn_forward for an upstream gradient dout (the
+ * training workload: the DSV explainer's speedups, "What it costs", are
+ * training numbers).  With P = softmax(z) of the forward (same selected
+ * blocks, same padding rules, P recomputed from lse):
+ *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = sm_scale dS K,  dK = sm_scale dS^T Q.
+ * bf16 only, head_dim = block = 128 (else SA_ERR_UNSUPPORTED).
+ * q, k, v: the forward's inputs, [H,q_rows,d] and full [H,kv_rows,d];
+ * out, lse: the forward's outputs for these inputs and blocks;
+ * dout: [H,q_rows,d], zero in padded rows;
+ * row_ptr, col_idx: the CSR of the forward; column ids ascending and unique
+ *   within each row (as sparse_attn_select / sparse_attn_csr_from_mask write);
+ * dq [H,q_rows,d], dk, dv [H,kv_rows,d]: out, bf16 (fp32 accumulation, P and
+ *   dS rounded to bf16 as MFMA operands); padded rows and key blocks that no
+ *   query block selected get zero;
+ * ws: workspace of sa_workspace_size(SA_STAGE_BACKWARD) bytes (D, and the
+ *   transposed block lists: per key block the query blocks that selected it). */
+int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse,
+                         const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
+                         void* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- video-aware block organisation --------------------------------------
  * The Top-p sparse-attention abstract (mlsift listing, tag "sequence
  * parallelism") organises video tokens into blocks in a video-aware way; the
@@ -217,7 +240,8 @@ int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 2 (1 plus the video block order entry points). */
+/* ABI version of this header: 3 (1, plus the video block order entry points
+ * in 2, plus sparse_attn_backward in 3). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

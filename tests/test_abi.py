@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 2
+    assert lib.sa_abi_version() == 3
 
 
 def test_struct_layout_matches_c():
@@ -186,3 +186,28 @@ def test_permute_rows_validation(lib):
     assert f(2, 10, 256, FAKE, FAKE + 2, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
     assert f(2, -1, 256, FAKE, FAKE, 10, FAKE, 16, None) == B.SA_ERR_INVALID_ARG
     assert f(2, 0, 256, None, None, 0, FAKE, 0, None) == B.SA_OK                   # nothing to do
+
+
+def test_backward_validation(lib):
+    f = B.load().sparse_attn_backward
+    prob = good_problem()
+    st, need = status_of_ws(prob, B.SA_STAGE_BACKWARD)
+    assert st == B.SA_OK and need > 0
+    args = [FAKE] * 11
+    ws = FAKE
+
+    def call(p, a, ws_bytes=need):
+        return f(ctypes.byref(p), *a, ws, ws_bytes, None)
+    assert call(good_problem(dtype=B.SA_F32), args) == B.SA_ERR_UNSUPPORTED
+    assert call(good_problem(head_dim=64), args) == B.SA_ERR_UNSUPPORTED
+    for n in range(11):
+        bad = list(args)
+        bad[n] = None
+        assert call(prob, bad) == B.SA_ERR_INVALID_ARG, n
+    bad = list(args)
+    bad[5] = FAKE + 4                     # lse not 16-byte aligned
+    assert call(prob, bad) == B.SA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[0] = FAKE + 8                     # q not 16-byte aligned
+    assert call(prob, bad) == B.SA_ERR_INVALID_ARG
+    assert call(prob, args, need - 1) == B.SA_ERR_WORKSPACE
