@@ -50,6 +50,9 @@ def parse():
                     help="video-aware block organisation: Q, K, V are gathered into 3-D tile "
                          "order before select and O, LSE back to raster order after forward "
                          "(both inside the timed step)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time sparse_attn_backward after each step (reported apart from "
+                         "the forward path's value)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device copy of MIB MiB (untimed), the "
                          "known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE counters")
@@ -141,6 +144,13 @@ def main():
     else:
         sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
     packed = not args.unpacked
+    if args.backward:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        dout = torch.randn(d["q"].shape, generator=g, device="cuda").to(d["q"].dtype)
+        dout[:, w.q_valid:] = 0
+        grads = [torch.empty_like(t) for t in (sa.q, sa.k, sa.v)]
+        bwd_ws_bytes = binding.sa_workspace_size(sa.prob, binding.SA_STAGE_BACKWARD)
+        bwd_ws = torch.empty(max(bwd_ws_bytes, 1), dtype=torch.uint8, device="cuda")
     flush = None if args.no_flush else (
         torch.empty(512 << 20, dtype=torch.uint8, device="cuda"),
         torch.zeros(64 << 20, dtype=torch.int64, device="cuda"))
@@ -163,6 +173,10 @@ def main():
             lay.to_raster(sa.out, w.q_rows, out=out_r)
             lay.to_raster(sa.lse.unsqueeze(-1), w.q_rows, out=lse_r)
         ev[5].record()
+        if args.backward:
+            binding.sparse_attn_backward(sa.prob, sa.q, sa.k, sa.v, sa.out, dout, sa.lse,
+                                         sa.row_ptr, sa.col_idx, *grads, bwd_ws, bwd_ws_bytes)
+        ev[6].record()
 
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
@@ -172,7 +186,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -193,6 +207,7 @@ def main():
     pck = np.array([e[2].elapsed_time(e[3]) for e in evs])
     fwd = np.array([e[3].elapsed_time(e[4]) for e in evs])
     pout = np.array([e[4].elapsed_time(e[5]) for e in evs])
+    bwd = np.array([e[5].elapsed_time(e[6]) for e in evs])
     tot = pin + sel + pck + fwd + pout
     nnz = sa.nnz()
     dense_pairs = w.heads * w.n_qb * w.n_kb
@@ -244,6 +259,14 @@ def main():
                      "kernel": "sparse_attn_forward (work-queue sort + attention)"},
         "wall_s_timed_region": round(wall, 3),
     }
+    if args.backward:
+        bflops = 10.0 * w.block * w.block * w.head_dim * nnz   # dS, dP, dV, dK, dQ GEMMs
+        bms = float(bwd.mean())
+        rec["backward"] = {
+            "ms": round(bms, 4), "tflop": round(bflops / 1e12, 4),
+            "tflops": round(bflops / (bms / 1e3) / 1e12, 3),
+            "frac_of_peak": round(bflops / (bms / 1e3) / 1e12 / peak, 4),
+            "flops_counted": "10*B^2*d per selected pair (five GEMMs; recomputed S and dP not counted)"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items)
     print(json.dumps(rec), flush=True)

@@ -348,7 +348,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
 # ---------------------------------------------------------------------------
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
                        q_valid: int, kv_valid: int, block: int, sm_scale: float,
-                       dout: np.ndarray, dtype=np.float64):
+                       dout: np.ndarray, dtype=np.float64,
+                       items: Optional[Sequence[tuple]] = None):
     """Gradients of `attention` (same mask, same padding rules) for an
     upstream gradient dO.  The DSV explainer's speedups are training numbers
     ("What it costs"), so the sparse attention is differentiated: with
@@ -358,35 +359,36 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.nda
     O is this oracle's own forward.  Padded query rows and rows with nothing
     selected contribute nothing; keys at or past kv_valid get zero gradient.
     Computed per (head, query block) in ``dtype``; returns dQ, dK, dV shaped
-    like q, k, v."""
+    like q, k, v.  items: optional list of (h, i) chunks to include; dQ rows
+    of other chunks stay 0, and dK, dV get only the listed chunks' terms."""
     H, q_rows, d = q.shape
     nqb = q_rows // block
     dq = np.zeros(q.shape, dtype)
     dk = np.zeros(k.shape, dtype)
     dv = np.zeros(v.shape, dtype)
     key_ok = np.arange(k.shape[1]) < kv_valid
-    for h in range(H):
+    todo = [(h, i) for h in range(H) for i in range(nqb)] if items is None else items
+    for h, i in todo:
         kh, vh = k[h].astype(dtype), v[h].astype(dtype)
-        for i in range(nqb):
-            lo, hi = i * block, min((i + 1) * block, q_valid)
-            if hi <= lo:
-                continue
-            allowed = np.repeat(mask[h, i], block) & key_ok
-            if not allowed.any():
-                continue
-            qc = q[h, lo:hi].astype(dtype)
-            go = dout[h, lo:hi].astype(dtype)
-            z = np.matmul(qc, kh.T) * dtype(sm_scale)
-            z[:, ~allowed] = -np.inf
-            e = np.exp(z - z.max(axis=1, keepdims=True))
-            p = e / e.sum(axis=1, keepdims=True)
-            o = np.matmul(p, vh)
-            dp = np.matmul(go, vh.T)
-            dd = (go * o).sum(axis=1, keepdims=True)
-            ds = p * (dp - dd)
-            dq[h, lo:hi] = dtype(sm_scale) * np.matmul(ds, kh)
-            dk[h] += dtype(sm_scale) * np.matmul(ds.T, qc)
-            dv[h] += np.matmul(p.T, go)
+        lo, hi = i * block, min((i + 1) * block, q_valid)
+        if hi <= lo:
+            continue
+        allowed = np.repeat(mask[h, i], block) & key_ok
+        if not allowed.any():
+            continue
+        qc = q[h, lo:hi].astype(dtype)
+        go = dout[h, lo:hi].astype(dtype)
+        z = np.matmul(qc, kh.T) * dtype(sm_scale)
+        z[:, ~allowed] = -np.inf
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        o = np.matmul(p, vh)
+        dp = np.matmul(go, vh.T)
+        dd = (go * o).sum(axis=1, keepdims=True)
+        ds = p * (dp - dd)
+        dq[h, lo:hi] = dtype(sm_scale) * np.matmul(ds, kh)
+        dk[h] += dtype(sm_scale) * np.matmul(ds.T, qc)
+        dv[h] += np.matmul(p.T, go)
     return dq, dk, dv
 
 

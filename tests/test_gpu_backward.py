@@ -30,32 +30,33 @@ def gpu():
     B.load()
 
 
-def bounds(x, mask, w, dout, o_bf):
-    """Per-element tolerances of dQ, dK, dV (fp64), following the docstring."""
+def bounds(x, mask, w, dout, o_bf, items=None):
+    """Per-element tolerances of dQ, dK, dV (fp64), following the docstring;
+    items: only these (h, i) chunks' terms."""
     q, k, v = x["q"].astype(np.float64), x["k"].astype(np.float64), x["v"].astype(np.float64)
     c = w.eff_sm_scale
     u = 2.0 ** -8
     tq, tk, tv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     key_ok = np.arange(k.shape[1]) < w.kv_valid
-    for h in range(w.heads):
-        for i in range(w.n_qb):
-            lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
-            if hi <= lo:
-                continue
-            allowed = np.repeat(mask[h, i], w.block) & key_ok
-            if not allowed.any():
-                continue
-            z = q[h, lo:hi] @ k[h].T * c
-            z[:, ~allowed] = -np.inf
-            e = np.exp(z - z.max(axis=1, keepdims=True))
-            p = e / e.sum(axis=1, keepdims=True)
-            go = dout[h, lo:hi].astype(np.float64)
-            o = p @ v[h]
-            ds = p * (go @ v[h].T - (go * o).sum(axis=1, keepdims=True))
-            dd = 2.0 ** -9 * (np.abs(go) * np.abs(o_bf[h, lo:hi])).sum(axis=1, keepdims=True)
-            tv[h] += u * (p.T @ np.abs(go))
-            tq[h, lo:hi] += c * (u * (np.abs(ds) @ np.abs(k[h])) + dd * (p @ np.abs(k[h])))
-            tk[h] += c * (u * (np.abs(ds).T @ np.abs(q[h, lo:hi])) + p.T @ (dd * np.abs(q[h, lo:hi])))
+    todo = [(h, i) for h in range(w.heads) for i in range(w.n_qb)] if items is None else items
+    for h, i in todo:
+        lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
+        if hi <= lo:
+            continue
+        allowed = np.repeat(mask[h, i], w.block) & key_ok
+        if not allowed.any():
+            continue
+        z = q[h, lo:hi] @ k[h].T * c
+        z[:, ~allowed] = -np.inf
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        go = dout[h, lo:hi].astype(np.float64)
+        o = p @ v[h]
+        ds = p * (go @ v[h].T - (go * o).sum(axis=1, keepdims=True))
+        dd = 2.0 ** -9 * (np.abs(go) * np.abs(o_bf[h, lo:hi])).sum(axis=1, keepdims=True)
+        tv[h] += u * (p.T @ np.abs(go))
+        tq[h, lo:hi] += c * (u * (np.abs(ds) @ np.abs(k[h])) + dd * (p @ np.abs(k[h])))
+        tk[h] += c * (u * (np.abs(ds).T @ np.abs(q[h, lo:hi])) + p.T @ (dd * np.abs(q[h, lo:hi])))
     return tq, tk, tv
 
 
@@ -156,3 +157,56 @@ def test_backward_deterministic_and_empty_rows():
     check(got, ref, bounds(x, m, w, dout, o_bf.double().numpy()))
     assert np.all(got[0][0, w.block:2 * w.block] == 0)
     assert np.all(got[1][1, 2 * w.block:3 * w.block] == 0)
+
+
+def test_backward_full_size_sampled():
+    """480p at full size, after the GPU's own select and forward.  Checked: dQ
+    of sampled query blocks, and dK, dV of one key block over every query
+    block that selected it.  For those query blocks the backward gets the
+    oracle's O and LSE (the other rows keep the GPU forward's), so each
+    checked gradient depends on oracle-provided forward outputs only."""
+    from test_gpu_fullsize import sampled_items
+    w = I.named("480p")
+    say("backward full size", w.name)
+    x = I.generate(w)
+    d = to_device(x, w)
+    sa = SparseAttention(w, d["q"], d["k"], d["v"])
+    sa.run(packed=True)
+    torch.cuda.synchronize()
+    mask = O.bits_to_mask(sa.mask_bits.cpu().numpy().view(np.uint32), w.heads, w.n_qb, w.n_kb)
+    rp, _ = sa.host_csr()
+    h0, j0 = 5, w.n_kb // 2
+    col_items = [(h0, i) for i in range(w.n_qb) if mask[h0, i, j0]]
+    items = sorted(set(col_items) | set(sampled_items(w, rp, n_random=3)))
+    say(f"  {len(col_items)} query blocks select key block ({h0}, {j0}); {len(items)} items")
+    rng = np.random.default_rng(1100)
+    dout = rng.standard_normal((w.heads, w.q_rows, w.head_dim)).astype(np.float32)
+    dout[:, w.q_valid:] = 0
+    dout = torch.from_numpy(dout).to(torch.bfloat16).float().numpy()
+    o_ref, lse_ref = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
+                                 w.eff_sm_scale, items=items, dtype=np.float64)
+    out_in = sa.out.clone()
+    lse_in = sa.lse.clone()
+    o_bf = torch.from_numpy(o_ref).to(torch.bfloat16)
+    for h, i in items:
+        sl = slice(i * w.block, (i + 1) * w.block)
+        out_in[h, sl] = o_bf[h, sl].cuda()
+        lse_in[h, sl] = torch.from_numpy(lse_ref[h, sl].astype(np.float32)).cuda()
+    dq = torch.empty_like(d["q"]); dk = torch.empty_like(d["k"]); dv = torch.empty_like(d["v"])
+    nbytes = B.sa_workspace_size(sa.prob, B.SA_STAGE_BACKWARD)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    B.sparse_attn_backward(sa.prob, d["q"], d["k"], d["v"], out_in, torch.from_numpy(dout).to(
+        torch.bfloat16).cuda(), lse_in, sa.row_ptr, sa.col_idx, dq, dk, dv, ws, nbytes)
+    torch.cuda.synchronize()
+    ref = O.attention_backward(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
+                               w.eff_sm_scale, dout, items=items)
+    tol = bounds(x, mask, w, dout, o_bf.double().numpy(), items=items)
+    rows = np.concatenate([np.arange(i * w.block, (i + 1) * w.block) for _, i in items])
+    heads = np.concatenate([np.full(w.block, h) for h, _ in items])
+    kb = slice(j0 * w.block, (j0 + 1) * w.block)
+    got = [dq.float().cpu().numpy()[heads, rows], dk.float().cpu().numpy()[h0, kb],
+           dv.float().cpu().numpy()[h0, kb]]
+    want = [ref[0][heads, rows], ref[1][h0, kb], ref[2][h0, kb]]
+    lim = [tol[0][heads, rows], tol[1][h0, kb], tol[2][h0, kb]]
+    worst = check(got, want, lim)
+    say(f"  max err / bound: dQ {worst[0]:.3f} dK {worst[1]:.3f} dV {worst[2]:.3f}")

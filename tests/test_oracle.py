@@ -655,3 +655,17 @@ def test_backward_key_gradients_sum_to_zero():
     mask = _random_mask(38, H=H, nqb=3, nkb=4, density=0.6)
     _, dk, _ = O.attention_backward(q, k, v, mask, 48, 64, B, 0.3, dout)
     np.testing.assert_allclose(dk.sum(axis=1), 0, atol=1e-12)
+
+
+def test_backward_items_partition_adds_up():
+    H, B, d = 2, 8, 4
+    q, k, v = _qkv(39, H, 24, 32, d)
+    dout = np.random.default_rng(40).standard_normal((H, 24, d)).astype(np.float32)
+    mask = _random_mask(41, H=H, nqb=3, nkb=4, density=0.6)
+    full = O.attention_backward(q, k, v, mask, 24, 30, B, 0.5, dout)
+    part_a = [(0, 0), (1, 2), (0, 2)]
+    part_b = [(0, 1), (1, 0), (1, 1)]
+    ga = O.attention_backward(q, k, v, mask, 24, 30, B, 0.5, dout, items=part_a)
+    gb = O.attention_backward(q, k, v, mask, 24, 30, B, 0.5, dout, items=part_b)
+    for f, a, b in zip(full, ga, gb):
+        np.testing.assert_allclose(f, a + b, atol=1e-12)
