@@ -92,12 +92,13 @@ PackWs pack_ws(const Dims& g) {
 }
 size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * sa::queue_words(g.H * g.nqb)); }
 struct BackwardWs {
-  size_t delta, counts, col_ptr, row_idx, total;
+  size_t delta, bits, counts, col_ptr, row_idx, total;
 };
 BackwardWs backward_ws(const Dims& g) {
   BackwardWs w{};
   size_t o = 0;
   w.delta = o; o += round_up(sizeof(float) * g.H * g.q_rows);
+  w.bits = o; o += round_up(sizeof(uint32_t) * g.H * g.nqb * g.W);
   w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nkb);
   w.col_ptr = o; o += round_up(sizeof(int32_t) * (g.H * g.nkb + 1));
   w.row_idx = o; o += round_up(sizeof(int32_t) * (size_t)g.H * g.nqb * g.nkb);
@@ -279,7 +280,8 @@ int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, c
   const BackwardWs w = backward_ws(g);
   const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
   SA_TRY_HIP(sa::launch_backward(g, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv,
-                                 at<float>(ws, w.delta), at<int32_t>(ws, w.counts),
+                                 at<float>(ws, w.delta), at<uint32_t>(ws, w.bits),
+                                 at<int32_t>(ws, w.counts),
                                  at<int32_t>(ws, w.col_ptr), at<int32_t>(ws, w.row_idx), sm,
                                  static_cast<hipStream_t>(stream)));
   return SA_OK;

@@ -6,12 +6,16 @@
 // P is recomputed from the forward's LSE, never stored.
 //
 //   delta_kernel    D per query row (fp32), one wave per row
-//   csc_*_kernel    the transpose of the CSR block lists (per key block, the
-//                   query blocks that selected it, ascending): count, scan, fill
+//   row_bits_kernel the block mask rebuilt from the CSR (one wave per row)
+//   csc_*_kernel    the transpose of the block lists (per key block, the query
+//                   blocks that selected it, ascending): count, scan, fill
 //   bwd_dq_kernel   one workgroup per (head, query block): over its CSR row,
-//                   S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//                   dP^T = V dO^T, then S^T = K Q^T, dS^T, dQ^T += K^T dS^T;
+//                   the next V loads during the K phase and the next K during
+//                   the next V phase
 //   bwd_dkdv_kernel one workgroup per (head, key block): over its CSC column,
-//                   S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
+//                   S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS;
+//                   two LDS buffers, the next query block loads during compute
 // All GEMMs are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
 // rounded to bf16 as MFMA operands.  Blocks arrive in LDS through direct loads
 // with the K swizzle (logical 16-byte chunk c of row r at c ^ (r & 15)); the
@@ -48,28 +52,48 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
   if (lane == 0) delta[row] = s;
 }
 
-// is key block j in CSR row [e0, e1) (ascending, unique ids)?
-__device__ __forceinline__ bool in_row(const int32_t* __restrict__ col_idx, int e0, int e1, int j) {
-  while (e0 < e1) {
-    const int m = (e0 + e1) >> 1;
-    const int c = col_idx[m];
-    if (c == j) return true;
-    if (c < j) e0 = m + 1; else e1 = m;
+// The block mask rebuilt from the CSR: one wave per row ORs its column ids
+// into LDS words (ids outside [0, nkb) are ignored), then writes the row.
+constexpr int kBitsWaves = 4;
+constexpr int kMaxWords = 4096 / 32;
+__global__ __launch_bounds__(kBitsWaves * kWave) void row_bits_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int rows, int nkb,
+    int W, uint32_t* __restrict__ bits) {
+  __shared__ uint32_t words[kBitsWaves][kMaxWords];
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r = blockIdx.x * kBitsWaves + wv;
+  if (r >= rows) return;   // whole wave; no workgroup barrier below
+  for (int w = lane; w < W; w += kWave) words[wv][w] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  const int e1 = row_ptr[r + 1];
+  for (int e = row_ptr[r] + lane; e < e1; e += kWave) {
+    const int j = col_idx[e];
+    if ((unsigned)j < (unsigned)nkb) atomicOr(&words[wv][j >> 5], 1u << (j & 31));
   }
-  return false;
+  __builtin_amdgcn_wave_barrier();
+  for (int w = lane; w < W; w += kWave) bits[(int64_t)r * W + w] = words[wv][w];
 }
 
-__global__ __launch_bounds__(256) void csc_count_kernel(const int32_t* __restrict__ row_ptr,
-                                                        const int32_t* __restrict__ col_idx, int H,
-                                                        int nqb, int nkb, int32_t* __restrict__ counts) {
+// per key block (h, j): the query blocks i whose mask row has bit j, ascending;
+// count only (fill == false) or write them at col_ptr (fill == true)
+template <bool kFill>
+__global__ __launch_bounds__(256) void csc_kernel(const uint32_t* __restrict__ bits, int H,
+                                                  int nqb, int nkb, int W,
+                                                  const int32_t* __restrict__ col_ptr,
+                                                  int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ row_idx) {
   for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < H * nkb; u += gridDim.x * blockDim.x) {
     const int h = u / nkb, j = u % nkb;
-    int c = 0;
+    const uint32_t* b = bits + (int64_t)h * nqb * W + (j >> 5);
+    const uint32_t m = 1u << (j & 31);
+    int c = 0, o = kFill ? col_ptr[u] : 0;
+#pragma unroll 8
     for (int i = 0; i < nqb; ++i) {
-      const int r = h * nqb + i;
-      c += in_row(col_idx, row_ptr[r], row_ptr[r + 1], j) ? 1 : 0;
+      const bool hit = (b[(int64_t)i * W] & m) != 0;
+      if (kFill && hit) row_idx[o + c] = i;
+      c += hit ? 1 : 0;
     }
-    counts[u] = c;
+    if (!kFill) counts[u] = c;
   }
 }
 
@@ -88,21 +112,6 @@ __global__ __launch_bounds__(kScanThreads) void csc_scan_kernel(const int32_t* _
     __syncthreads();
   }
   if (threadIdx.x == 0) col_ptr[n] = base;
-}
-
-__global__ __launch_bounds__(256) void csc_fill_kernel(const int32_t* __restrict__ row_ptr,
-                                                       const int32_t* __restrict__ col_idx, int H,
-                                                       int nqb, int nkb,
-                                                       const int32_t* __restrict__ col_ptr,
-                                                       int32_t* __restrict__ row_idx) {
-  for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < H * nkb; u += gridDim.x * blockDim.x) {
-    const int h = u / nkb, j = u % nkb;
-    int o = col_ptr[u];
-    for (int i = 0; i < nqb; ++i) {
-      const int r = h * nqb + i;
-      if (in_row(col_idx, row_ptr[r], row_ptr[r + 1], j)) row_idx[o++] = i;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -189,35 +198,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
 
+  // Per block j (V_j landed, K_j in flight at the top):
+  //   dP^T = V dO^T (V rows); wait for K_j, barrier; load V_{j+1};
+  //   S^T = K Q^T, dS^T, dQ^T += K^T dS^T (K rows, K transposed);
+  //   wait for V_{j+1}, barrier; load K_{j+1}.
   const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[item]);
   const int e1 = __builtin_amdgcn_readfirstlane(row_ptr[item + 1]);
-  for (int e = e0; e < e1; ++e) {
+  auto src_of = [&](int e) -> int64_t {   // block offset of entry e, -1 if outside the row
     const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
-    if ((unsigned)j >= (unsigned)nkb) continue;
-    const int64_t src = ((int64_t)h * kv_rows + (int64_t)j * kB) * kD;
-    __syncthreads();   // previous block's tiles are no longer read
-    dma_block(k + src, kl, wave, off.dma);
+    return (unsigned)j < (unsigned)nkb ? ((int64_t)h * kv_rows + (int64_t)j * kB) * kD : -1;
+  };
+  int e = e0;
+  int64_t src = -1;
+  while (e < e1 && (src = src_of(e)) < 0) ++e;
+  if (e < e1) {
     dma_block(v + src, vl, wave, off.dma);
-    __builtin_amdgcn_s_waitcnt(0);
+    dma_block(k + src, kl, wave, off.dma);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (e < e1) {
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
+    int en = e + 1;
+    int64_t sn = -1;
+    while (en < e1 && (sn = src_of(en)) < 0) ++en;
+    f32x16 dpacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpacc[t][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dpacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(vl, off, t, s), df[s], dpacc[t],
+                                                           0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's K_j loads
     __syncthreads();
+    if (en < e1) dma_block(v + sn, vl, wave, off.dma);
     const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      f32x16 sacc, dpacc;
+      f32x16 sacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dpacc[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 8; ++s)
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(kl, off, t, s), qf[s], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(vl, off, t, s), df[s], dpacc, 0, 0, 0);
-      }
       // reg r: key 32t + 8(r/4) + 4g + r%4 of this lane's query
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
         const float p = key < lim ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
-        ds[r] = p * (dpacc[r] - dlt);
+        ds[r] = p * (dpacc[t][r] - dlt);
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -228,6 +261,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                                                            0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's V_{j+1} loads
+    __syncthreads();
+    if (en < e1) dma_block(k + sn, kl, wave, off.dma);
+    e = en;
   }
   // dQ[query][d], reg r of tile u -> d = 32u + 8(r/4) + 4g + r%4
   uint16_t* op = dq + (qbase + qrow) * kD;
@@ -250,10 +287,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int nqb, int nkb, int64_t q_rows,
     int64_t q_valid, int64_t kv_rows, int64_t kv_valid, float scale_log2, float sm_scale) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ql[kB * kD];
-  __shared__ __attribute__((aligned(1024))) uint16_t dl[kB * kD];
-  __shared__ __attribute__((aligned(16))) float lse_s[kB];
-  __shared__ __attribute__((aligned(16))) float dlt_s[kB];
+  // two buffers: the next query block loads while this one is computed
+  __shared__ __attribute__((aligned(1024))) uint16_t qbuf[2][kB * kD];
+  __shared__ __attribute__((aligned(1024))) uint16_t dbuf[2][kB * kD];
+  __shared__ __attribute__((aligned(16))) float lse_b[2][kB];
+  __shared__ __attribute__((aligned(16))) float dlt_b[2][kB];
   const int unit = blockIdx.x;
   const int h = unit / nkb, j = unit % nkb;
   const int tid = threadIdx.x;
@@ -277,20 +315,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int c0 = __builtin_amdgcn_readfirstlane(col_ptr[unit]);
   const int c1 = __builtin_amdgcn_readfirstlane(col_ptr[unit + 1]);
-  for (int c = c0; c < c1; ++c) {
+  // query block i of column entry c into buffer b (Q, dO by direct loads;
+  // LSE in log2 units, +inf for rows without attention so P = 0; D)
+  auto stage = [&](int c, int b) {
     const int i = __builtin_amdgcn_readfirstlane(row_idx[c]);
     const int64_t qb = (int64_t)h * q_rows + (int64_t)i * kB;
-    __syncthreads();   // previous query block's tiles are no longer read
-    dma_block(q + qb * kD, ql, wave, off.dma);
-    dma_block(dout + qb * kD, dl, wave, off.dma);
+    dma_block(q + qb * kD, qbuf[b], wave, off.dma);
+    dma_block(dout + qb * kD, dbuf[b], wave, off.dma);
     if (tid < kB) {
       const int64_t row = (int64_t)i * kB + tid;
       const float l = lse[qb + tid];
-      lse_s[tid] = (row < q_valid && l > -INFINITY) ? l * kLog2e : INFINITY;   // +inf: P = 0
-      dlt_s[tid] = delta[qb + tid];
+      lse_b[b][tid] = (row < q_valid && l > -INFINITY) ? l * kLog2e : INFINITY;
+      dlt_b[b][tid] = delta[qb + tid];
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  if (c0 < c1) stage(c0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c = c0, b = 0; c < c1; ++c, b ^= 1) {
+    if (c + 1 < c1) stage(c + 1, b ^ 1);   // that buffer was last read before the barrier
+    const uint16_t* ql = qbuf[b];
+    const uint16_t* dl = dbuf[b];
+    const float* lse_s = lse_b[b];
+    const float* dlt_s = dlt_b[b];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x16 sacc, dpacc;
@@ -330,6 +377,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next block
+    __syncthreads();
   }
   // dK, dV [key][d], reg r of tile u -> d = 32u + 8(r/4) + 4g + r%4
   uint16_t* kp = dk + (kbase + krow) * kD;
@@ -355,19 +404,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 hipError_t launch_backward(const Dims& g, const void* q, const void* k, const void* v,
                            const void* out, const void* dout, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
-                           void* dv, float* delta, int32_t* counts, int32_t* col_ptr,
-                           int32_t* row_idx, float sm_scale, hipStream_t s) {
+                           void* dv, float* delta, uint32_t* bits, int32_t* counts,
+                           int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s) {
   const int64_t qrows_total = (int64_t)g.H * g.q_rows;
   hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((qrows_total + 3) / 4)), dim3(256), 0, s,
                      (const uint16_t*)out, (const uint16_t*)dout, qrows_total, g.q_rows,
                      g.q_valid, delta);
   const int cols = g.H * g.nkb;
+  const int rows = g.H * g.nqb;
+  hipLaunchKernelGGL(row_bits_kernel, dim3((rows + kBitsWaves - 1) / kBitsWaves),
+                     dim3(kBitsWaves * kWave), 0, s, row_ptr, col_idx, rows, g.nkb, g.W, bits);
   const int grid = std::min((cols + 255) / 256, 1024);
-  hipLaunchKernelGGL(csc_count_kernel, dim3(grid), dim3(256), 0, s, row_ptr, col_idx, g.H, g.nqb,
-                     g.nkb, counts);
+  hipLaunchKernelGGL(csc_kernel<false>, dim3(grid), dim3(256), 0, s, bits, g.H, g.nqb, g.nkb,
+                     g.W, (const int32_t*)nullptr, counts, (int32_t*)nullptr);
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, cols, col_ptr);
-  hipLaunchKernelGGL(csc_fill_kernel, dim3(grid), dim3(256), 0, s, row_ptr, col_idx, g.H, g.nqb,
-                     g.nkb, col_ptr, row_idx);
+  hipLaunchKernelGGL(csc_kernel<true>, dim3(grid), dim3(256), 0, s, bits, g.H, g.nqb, g.nkb,
+                     g.W, col_ptr, (int32_t*)nullptr, row_idx);
   const float scale_log2 = sm_scale * kLog2e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(g.H * g.nqb), dim3(256), 0, s, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, delta,

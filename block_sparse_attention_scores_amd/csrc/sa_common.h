@@ -127,6 +127,6 @@ hipError_t launch_permute_rows(int heads, int64_t rows, int row_bytes, const int
 hipError_t launch_backward(const Dims& g, const void* q, const void* k, const void* v,
                            const void* out, const void* dout, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
-                           void* dv, float* delta, int32_t* counts, int32_t* col_ptr,
-                           int32_t* row_idx, float sm_scale, hipStream_t s);
+                           void* dv, float* delta, uint32_t* bits, int32_t* counts,
+                           int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s);
 }  // namespace sa
