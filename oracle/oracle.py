@@ -102,6 +102,36 @@ def block_scores_lowrank(qbar: np.ndarray, kbar: np.ndarray,
     return np.matmul(qt, np.swapaxes(kt, 1, 2))
 
 
+def block_scores_lowrank_max(q: np.ndarray, k: np.ndarray, q_valid: int, kv_valid: int,
+                             block: int, wq: np.ndarray, wk: np.ndarray,
+                             items: Optional[Sequence[tuple]] = None) -> np.ndarray:
+    """Token-level variant of the rank-r predictor, fp64.
+
+    The DSV explainer ("The idea") predicts query-key scores token by token
+    with two small low-rank matrices and then picks the critical pairs.  This
+    variant keeps the token-level view inside each block pair: the block
+    score is the largest predicted token-pair score (q_a W_q) . (k_b W_k)
+    over the valid tokens a of query block i and b of key block j (instead of
+    the mean, which `block_scores_lowrank` gives).  q [H, q_rows, d],
+    k [H, kv_rows, d], wq, wk [H, d, r].  items: optional (h, i) rows to
+    compute (others are left NaN).  Returns [H, nQB, nKB].
+    """
+    H = q.shape[0]
+    nqb, nkb = q.shape[1] // block, k.shape[1] // block
+    s = np.full((H, nqb, nkb), np.nan)
+    todo = [(h, i) for h in range(H) for i in range(nqb)] if items is None else items
+    kt = {}
+    for h, i in todo:
+        if h not in kt:
+            kt[h] = np.matmul(k[h, :kv_valid].astype(np.float64), wk[h].astype(np.float64))
+        lo, hi = i * block, min((i + 1) * block, q_valid)
+        qt = np.matmul(q[h, lo:hi].astype(np.float64), wq[h].astype(np.float64))
+        pair = np.matmul(qt, kt[h].T)                     # [tokens of block i, kv_valid]
+        for j in range(nkb):
+            s[h, i, j] = pair[:, j * block:min((j + 1) * block, kv_valid)].max()
+    return s
+
+
 # ---------------------------------------------------------------------------
 # A4/A5: selection
 # ---------------------------------------------------------------------------
@@ -464,8 +494,10 @@ def scores_for(q, k, q_valid, kv_valid, block, score_mode, score_scale, wq=None,
     kbar = pool_means(k, kv_valid, block)
     if score_mode == 0:
         s = block_scores_pooled(qbar, kbar, score_scale)
-    else:
+    elif score_mode == 1:
         s = block_scores_lowrank(qbar, kbar, wq, wk)
+    else:
+        s = block_scores_lowrank_max(q, k, q_valid, kv_valid, block, wq, wk)
     return qbar, kbar, s
 
 

@@ -669,3 +669,73 @@ def test_backward_items_partition_adds_up():
     gb = O.attention_backward(q, k, v, mask, 24, 30, B, 0.5, dout, items=part_b)
     for f, a, b in zip(full, ga, gb):
         np.testing.assert_allclose(f, a + b, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# token-level low-rank predictor, max aggregation
+# ---------------------------------------------------------------------------
+def test_lowrank_max_by_token_pair_loops():
+    rng = np.random.default_rng(50)
+    H, B, d, r = 2, 4, 3, 2
+    q = rng.standard_normal((H, 12, d)).astype(np.float32)
+    k = rng.standard_normal((H, 16, d)).astype(np.float32)
+    qv, kv = 10, 13
+    q[:, qv:] = 0; k[:, kv:] = 0
+    wq = rng.standard_normal((H, d, r)).astype(np.float32)
+    wk = rng.standard_normal((H, d, r)).astype(np.float32)
+    s = O.block_scores_lowrank_max(q, k, qv, kv, B, wq, wk)
+    for h in range(H):
+        for i in range(3):
+            for j in range(4):
+                best = -math.inf
+                for a in range(i * B, min((i + 1) * B, qv)):
+                    for b in range(j * B, min((j + 1) * B, kv)):
+                        val = 0.0
+                        for c in range(r):
+                            qa = sum(float(q[h, a, e]) * float(wq[h, e, c]) for e in range(d))
+                            kb = sum(float(k[h, b, e]) * float(wk[h, e, c]) for e in range(d))
+                            val += qa * kb
+                        best = max(best, val)
+                assert abs(s[h, i, j] - best) <= 1e-12 * max(1.0, abs(best))
+
+
+def test_lowrank_max_rank_one_closed_form_and_padding():
+    rng = np.random.default_rng(51)
+    B, d = 8, 4
+    q = rng.standard_normal((1, 16, d)).astype(np.float32)
+    k = rng.standard_normal((1, 24, d)).astype(np.float32)
+    wq = rng.standard_normal((1, d, 1)).astype(np.float32)
+    wk = rng.standard_normal((1, d, 1)).astype(np.float32)
+    qv, kv = 13, 20
+    q[:, qv:] = 0; k[:, kv:] = 0
+    s = O.block_scores_lowrank_max(q, k, qv, kv, B, wq, wk)
+    x = q[0].astype(np.float64) @ wq[0, :, 0].astype(np.float64)
+    y = k[0].astype(np.float64) @ wk[0, :, 0].astype(np.float64)
+    for i in range(2):
+        xs = x[i * B:min((i + 1) * B, qv)]
+        for j in range(3):
+            ys = y[j * B:min((j + 1) * B, kv)]
+            want = max(xs.max() * ys.max(), xs.min() * ys.min(), xs.max() * ys.min(), xs.min() * ys.max())
+            assert abs(s[0, i, j] - want) <= 1e-12 * max(1.0, abs(want))
+    # with every real score negative, padding (which would score 0) must not show
+    q2 = np.abs(q); k2 = -np.abs(k)
+    w1 = np.ones((1, d, 1), np.float32)
+    s2 = O.block_scores_lowrank_max(q2, k2, qv, kv, B, w1, w1)
+    assert np.all(s2 < 0)
+
+
+def test_lowrank_max_bounds_the_mean():
+    """The mean over the block pair (block_scores_lowrank) never exceeds the max."""
+    rng = np.random.default_rng(52)
+    H, B, d, r = 2, 16, 32, 4
+    q = rng.standard_normal((H, 64, d)).astype(np.float32)
+    k = rng.standard_normal((H, 96, d)).astype(np.float32)
+    q[:, 60:] = 0; k[:, 90:] = 0
+    wq = rng.standard_normal((H, d, r)).astype(np.float32)
+    wk = rng.standard_normal((H, d, r)).astype(np.float32)
+    smax = O.block_scores_lowrank_max(q, k, 60, 90, B, wq, wk)
+    smean = O.block_scores_lowrank(O.pool_means(q, 60, B), O.pool_means(k, 90, B), wq, wk)
+    assert np.all(smax >= smean - 1e-12)
+    rows = O.block_scores_lowrank_max(q, k, 60, 90, B, wq, wk, items=[(1, 2)])
+    np.testing.assert_array_equal(rows[1, 2], smax[1, 2])
+    assert np.isnan(rows[0, 0]).all()
