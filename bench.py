@@ -235,7 +235,7 @@ def main():
                    "block": w.block, "q_tokens": w.q_valid, "kv_tokens": w.kv_valid,
                    "latent_thw": list(w.latent), "top_p": w.top_p, "top_k": w.top_k,
                    "select_mode": "top_p" if w.select_mode == 0 else "top_k",
-                   "score": "pooled" if w.score_mode == 0 else f"lowrank{w.rank}",
+                   "score": ("pooled", f"lowrank{w.rank}", f"lowrank{w.rank}_tokenmax")[w.score_mode],
                    "packed_kv": packed, "cache": "warm" if flush is None else "flushed each step",
                    "layout": "tiles " + "x".join(map(str, tiles)) if tiles else "raster"},
         "ms_per_layer": round(ms_step, 4),

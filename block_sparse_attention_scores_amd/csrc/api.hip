@@ -44,8 +44,11 @@ int check_problem(const sa_problem* p, Dims* g) {
   if (p->select_mode == SA_TOP_P && !(p->top_p > 0.f)) return SA_ERR_INVALID_ARG;
   if (p->select_mode == SA_TOP_P && p->top_k < 0) return SA_ERR_INVALID_ARG;
   if (p->select_mode == SA_TOP_K && p->top_k < 1) return SA_ERR_INVALID_ARG;
-  if (p->score_mode != SA_SCORE_POOLED && p->score_mode != SA_SCORE_LOWRANK) return SA_ERR_INVALID_ARG;
-  if (p->score_mode == SA_SCORE_LOWRANK && (p->rank < 1 || p->rank > 64)) return SA_ERR_INVALID_ARG;
+  if (p->score_mode != SA_SCORE_POOLED && p->score_mode != SA_SCORE_LOWRANK &&
+      p->score_mode != SA_SCORE_LOWRANK_MAX)
+    return SA_ERR_INVALID_ARG;
+  if (p->score_mode != SA_SCORE_POOLED && (p->rank < 1 || p->rank > 64)) return SA_ERR_INVALID_ARG;
+  if (p->score_mode == SA_SCORE_LOWRANK_MAX && p->rank != 16) return SA_ERR_UNSUPPORTED;
   if (!isfinite(p->sm_scale) || !isfinite(p->score_scale)) return SA_ERR_INVALID_ARG;
   g->H = p->num_heads;
   g->d = p->head_dim;
@@ -54,6 +57,7 @@ int check_problem(const sa_problem* p, Dims* g) {
   g->nkb = (int)nkb;
   g->W = (int)((nkb + 31) / 32);
   g->rank = p->score_mode == SA_SCORE_LOWRANK ? p->rank : 0;
+  g->score_mode = p->score_mode;
   g->q_rows = p->q_rows;
   g->q_valid = p->q_valid;
   g->kv_rows = p->kv_rows;
@@ -64,7 +68,7 @@ int check_problem(const sa_problem* p, Dims* g) {
 
 // Workspace layout of every stage, in carve order.
 struct SelectWs {
-  size_t qbar, kbar, qt, kt, scores, counts, total;
+  size_t qbar, kbar, qt, kt, qtok, ktok, scores, counts, total;
 };
 SelectWs select_ws(const Dims& g) {
   SelectWs w{};
@@ -73,6 +77,9 @@ SelectWs select_ws(const Dims& g) {
   w.kbar = o; o += round_up(sizeof(double) * g.H * g.nkb * g.d);
   w.qt = o; o += round_up(sizeof(double) * g.H * g.nqb * g.rank);
   w.kt = o; o += round_up(sizeof(double) * g.H * g.nkb * g.rank);
+  const size_t tok = g.score_mode == SA_SCORE_LOWRANK_MAX ? 16 : 0;   // projected tokens
+  w.qtok = o; o += round_up(sizeof(float) * g.H * g.q_rows * tok);
+  w.ktok = o; o += round_up(sizeof(float) * g.H * g.kv_rows * tok);
   w.scores = o; o += round_up(sizeof(double) * g.H * g.nqb * g.nkb);
   w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nqb);
   w.total = o;
@@ -172,7 +179,7 @@ int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, con
   if (st != SA_OK) return st;
   if (!q || !k || !mask_bits || !row_ptr || !col_idx) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_INVALID_ARG;
-  if (g.rank > 0 && (!wq || !wk)) return SA_ERR_INVALID_ARG;
+  if (g.score_mode != SA_SCORE_POOLED && (!wq || !wk)) return SA_ERR_INVALID_ARG;
   if ((qbar_opt && ((uintptr_t)qbar_opt & 7u)) || (kbar_opt && ((uintptr_t)kbar_opt & 7u)))
     return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_SELECT, ws, ws_bytes);
@@ -187,7 +194,10 @@ int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, con
   int32_t* counts = at<int32_t>(ws, w.counts);
 
   SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
-  if (g.rank > 0) {
+  if (g.score_mode == SA_SCORE_LOWRANK_MAX) {
+    SA_TRY_HIP(sa::launch_lowrank_max(g, q, k, wq, wk, at<float>(ws, w.qtok),
+                                      at<float>(ws, w.ktok), scores, s));
+  } else if (g.rank > 0) {
     SA_TRY_HIP(sa::launch_scores(g, qt, kt, g.rank, 1.0, scores, s));
   } else {
     const double sc = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);

@@ -89,7 +89,8 @@ __device__ T block_inclusive_scan(T v, T* scratch, T* total) {
 // ---- host launchers (one per translation unit), used by api.hip ----------
 namespace sa {
 struct Dims {
-  int H, d, B, nqb, nkb, W, rank;
+  int H, d, B, nqb, nkb, W, rank;   // rank: of the projected block means (0: none)
+  int score_mode;
   int64_t q_rows, q_valid, kv_rows, kv_valid;
   int dtype;
 };
@@ -129,4 +130,7 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
                            void* dv, float* delta, uint32_t* bits, int32_t* counts,
                            int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s);
+hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const float* wq,
+                              const float* wk, float* qtok, float* ktok, double* scores,
+                              hipStream_t s);
 }  // namespace sa

@@ -45,6 +45,7 @@ SELECT_TOP_P = 0
 SELECT_TOP_K = 1
 SCORE_POOLED = 0
 SCORE_LOWRANK = 1
+SCORE_LOWRANK_MAX = 2   # token-level predicted scores, max over the block pair
 
 
 @dataclasses.dataclass(frozen=True)
@@ -153,8 +154,15 @@ def hetero() -> Workload:
                     strength_range=(0.05, 2.0), top_p=0.95, top_k=4)
 
 
+def lowrank_max() -> Workload:
+    """The low-rank workload with token-level predicted scores aggregated by
+    the max over each block pair (same inputs, same W, same top-k)."""
+    return dataclasses.replace(lowrank(), name="lowrank_tokenmax_128k",
+                               score_mode=SCORE_LOWRANK_MAX)
+
+
 NAMED = {"tiny": tiny, "480p": c480p, "720p_rank": c720p_rank,
-         "lowrank": lowrank, "hetero": hetero}
+         "lowrank": lowrank, "hetero": hetero, "lowrank_max": lowrank_max}
 
 
 def named(name: str) -> Workload:
@@ -240,7 +248,7 @@ def generate(w: Workload, heads: Optional[Sequence[int]] = None, threads: int = 
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(work, range(len(hs))))
     out = {"q": q, "k": k, "v": v}
-    if w.score_mode == SCORE_LOWRANK:
+    if w.score_mode != SCORE_POOLED:
         out["wq"], out["wk"] = lowrank_weights(w, hs)
     return out
 

@@ -12,7 +12,7 @@ from typing import Optional
 import torch
 
 from . import binding as B
-from .inputs import SCORE_LOWRANK, Workload
+from .inputs import SCORE_POOLED, Workload
 
 
 def problem_for(w: Workload) -> B.SaProblem:
@@ -69,7 +69,7 @@ class SparseAttention:
 
     def select(self):
         ws, n = self._ws(B.SA_STAGE_SELECT)
-        lowrank = self.w.score_mode == SCORE_LOWRANK
+        lowrank = self.w.score_mode != SCORE_POOLED
         B.sparse_attn_select(self.prob, self.q, self.k, self.wq if lowrank else None,
                              self.wk if lowrank else None, self.mask_bits, self.row_ptr,
                              self.col_idx, self.qbar, self.kbar, ws, n)

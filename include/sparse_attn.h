@@ -57,7 +57,12 @@ typedef enum sa_status {
 
 typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 typedef enum sa_select_mode { SA_TOP_P = 0, SA_TOP_K = 1 } sa_select_mode;
-typedef enum sa_score_mode { SA_SCORE_POOLED = 0, SA_SCORE_LOWRANK = 1 } sa_score_mode;
+typedef enum sa_score_mode {
+  SA_SCORE_POOLED = 0,      /* block means, scaled dot product                    */
+  SA_SCORE_LOWRANK = 1,     /* mean over the block pair of rank-r predicted scores */
+  SA_SCORE_LOWRANK_MAX = 2  /* max over the block pair of rank-16 predicted token
+                               scores (fp32 token scores; rank must be 16)         */
+} sa_score_mode;
 typedef enum sa_stage {
   SA_STAGE_SELECT = 0,   /* sparse_attn_select         */
   SA_STAGE_CSR = 1,      /* sparse_attn_csr_from_mask  */
@@ -86,7 +91,7 @@ typedef struct sa_problem {
   int32_t top_k;        /* SA_TOP_P: floor (>= 0); SA_TOP_K: k (>= 1); both
                            are clamped to nKB                                 */
   int32_t score_mode;   /* sa_score_mode                                      */
-  int32_t rank;         /* SA_SCORE_LOWRANK: predictor rank r, 1..64          */
+  int32_t rank;         /* low-rank modes: predictor rank r, 1..64 (16 for MAX) */
 } sa_problem;
 
 /* Workspace bytes needed by one entry point (`stage`) for this problem.
@@ -103,6 +108,10 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
  *   SA_SCORE_LOWRANK: S[h,i,j] = <qbar[h,i] Wq[h], kbar[h,j] Wk[h]>, i.e. the
  *                     mean over the block pair of the rank-r predicted
  *                     token-pair scores
+ *   SA_SCORE_LOWRANK_MAX: S[h,i,j] = max over valid tokens a of block i and b
+ *                     of block j of <q_a Wq[h], k_b Wk[h]> (rank 16; the
+ *                     projections are fp64 sums stored as fp32, the token-pair
+ *                     scores fp32 on the matrix cores, S their fp32 max)
  *   SA_TOP_P: P = softmax_j S[h,i,:]; blocks ordered by P descending, ties to
  *             the lower j; keep the shortest prefix whose cumulative mass
  *             reaches top_p (all blocks if top_p >= 1 or the prefix never
@@ -111,7 +120,7 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
  * All selection arithmetic is fp64.
  *
  * q [H,q_rows,d], k [H,kv_rows,d]: input dtype.
- * wq, wk: fp32 [H,d,rank] (SA_SCORE_LOWRANK only; else ignored, may be NULL).
+ * wq, wk: fp32 [H,d,rank] (the low-rank modes only; else ignored, may be NULL).
  * mask_bits: out, uint32 [H*nQB, W]; bit b of word w of row h*nQB+i is block
  *            32w+b; bits at or beyond nKB are 0.
  * row_ptr:   out, int32 [H*nQB+1], CSR row offsets (rows head-major).

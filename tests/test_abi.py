@@ -90,6 +90,9 @@ def test_workspace_sizes(lib):
     (dict(select_mode=5), B.SA_ERR_INVALID_ARG),
     (dict(score_mode=B.SA_SCORE_LOWRANK, rank=0), B.SA_ERR_INVALID_ARG),
     (dict(score_mode=B.SA_SCORE_LOWRANK, rank=65), B.SA_ERR_INVALID_ARG),
+    (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=8), B.SA_ERR_UNSUPPORTED),
+    (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=0), B.SA_ERR_INVALID_ARG),
+    (dict(score_mode=3), B.SA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), B.SA_ERR_INVALID_ARG),
 ])
 def test_problem_validation(lib, kw, expect):
@@ -115,6 +118,9 @@ def test_select_argument_errors(lib):
     lr = good_problem(score_mode=B.SA_SCORE_LOWRANK, rank=16)
     bad = list(args); bad[0] = ctypes.byref(lr)
     assert f(*bad) == B.SA_ERR_INVALID_ARG                     # low-rank without W
+    lm = good_problem(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=16)
+    bad = list(args); bad[0] = ctypes.byref(lm)
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # token max without W
 
 
 def test_pack_and_forward_argument_errors(lib):
@@ -151,9 +157,6 @@ def test_csr_argument_errors(lib):
     assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
     assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE * 4, 0, None) == B.SA_ERR_WORKSPACE
     assert f(None, FAKE, FAKE, FAKE, FAKE * 4, n, None) == B.SA_ERR_INVALID_ARG
-
-
-FAKE = 0x10000   # never dereferenced: every case below fails validation first
 
 
 def test_video_order_validation(lib):

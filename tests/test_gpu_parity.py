@@ -62,6 +62,7 @@ def check_selection(w, sa, x, rows_to_check=None):
     if nkb % 32:
         assert np.all(bits[:, -1] >> np.uint32(nkb % 32) == 0)
     excused = 0
+    rel = tokenmax_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MAX else None
     for h in range(w.heads):
         for i in range(w.n_qb):
             if w.select_mode == I.SELECT_TOP_P:
@@ -71,10 +72,35 @@ def check_selection(w, sa, x, rows_to_check=None):
             want = np.zeros(nkb, bool)
             want[rec.order[:rec.m]] = True
             if not np.array_equal(want, mask[h, i]):
-                assert O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, mask[h, i]), \
+                r = 1e-6 if rel is None else max(1e-6, float(rel[h, i]))
+                assert O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, mask[h, i],
+                                              rel=r), \
                     f"selection mismatch at head {h} query block {i}"
                 excused += 1
     return mask, excused
+
+
+def tokenmax_rel(w, x, s):
+    """Near-tie tolerance of the token-level max scores, per row.  The GPU
+    rounds the projected tokens to fp32 and forms each 16-term dot product in
+    fp32: its error is at most about 18 * 2^-24 * sum_c |q~_c k~_c| <= 2^-19 *
+    |q~_a| |k~_b| (doubled for margin), so a block score is within
+    delta = 2^-19 max_a |q~_a| max_b |k~_b| of the exact one.  Top-k compares
+    scores (relative to the row's max |S|), top-p softmax masses (relative
+    error up to 2 delta)."""
+    qt = np.matmul(x["q"][:, :w.q_valid].astype(np.float64), x["wq"].astype(np.float64))
+    kt = np.matmul(x["k"][:, :w.kv_valid].astype(np.float64), x["wk"].astype(np.float64))
+    qn = np.linalg.norm(qt, axis=2)
+    kn = np.linalg.norm(kt, axis=2).max(axis=1)                          # [H]
+    rel = np.zeros((w.heads, w.n_qb))
+    for i in range(w.n_qb):
+        lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
+        delta = 2.0 ** -19 * qn[:, lo:hi].max(axis=1) * kn
+        if w.select_mode == I.SELECT_TOP_K:
+            rel[:, i] = delta / np.abs(s[:, i]).max(axis=1)
+        else:
+            rel[:, i] = 2 * delta
+    return rel
 
 
 def check_csr_demand_pack(w, sa, mask, x):
@@ -181,6 +207,23 @@ def test_lowrank_top_k():
                    select_mode=I.SELECT_TOP_K, top_k=3, score_mode=I.SCORE_LOWRANK, seed=25)
     sa, _, mask = full_check(w)
     assert np.all(mask.sum(axis=2) == 3)
+
+
+@pytest.mark.parametrize("mode,p,k", [(I.SELECT_TOP_K, 0.9, 5), (I.SELECT_TOP_P, 0.6, 2)])
+def test_lowrank_token_max(mode, p, k):
+    """Token-level rank-16 predicted scores, max over each block pair."""
+    w = small_bf16(name="tokmax", heads=2, latent=(4, 16, 37), q_valid=700,
+                   select_mode=mode, top_p=p, top_k=k, score_mode=I.SCORE_LOWRANK_MAX, seed=71)
+    sa, _, mask = full_check(w)
+    if mode == I.SELECT_TOP_K:
+        assert np.all(mask.sum(axis=2) == min(k, w.n_kb))
+
+
+def test_f32_token_max_block_64():
+    w = I.Workload("tokmax_f32", heads=2, head_dim=64, block=64, dtype="f32", latent=(3, 10, 20),
+                   q_start=0, q_valid=450, seed=72, strength=1.0, tile=(1, 4, 4), clusters=4,
+                   select_mode=I.SELECT_TOP_K, top_k=3, score_mode=I.SCORE_LOWRANK_MAX)
+    full_check(w)
 
 
 def test_p_one_keeps_everything_and_equals_dense():
