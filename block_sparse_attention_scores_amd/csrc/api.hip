@@ -10,7 +10,6 @@
 
 namespace sa {
 bool attn_supported(int dtype, int d, int B);
-int queue_words(int rows);
 }
 
 namespace {
@@ -97,7 +96,7 @@ PackWs pack_ws(const Dims& g) {
   w.total = o;
   return w;
 }
-size_t forward_ws(const Dims& g) { return round_up(sizeof(int32_t) * sa::queue_words(g.H * g.nqb)); }
+size_t forward_ws(const Dims& g) { return round_up(sa::attn_ws_bytes(g)); }
 struct BackwardWs {
   size_t delta, bits, counts, col_ptr, row_idx, total;
 };
@@ -264,11 +263,9 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
   st = check_ws(g, SA_STAGE_FORWARD, ws, ws_bytes);
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* items = static_cast<int32_t*>(ws);
   const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
-  SA_TRY_HIP(sa::launch_queue(g, row_ptr, items, s));
-  SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, items,
-                             sm, s));
+  SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
+                             ws_bytes, sm, s));
   return SA_OK;
 }
 

@@ -36,36 +36,82 @@ using namespace bf16mma;
 // ---------------------------------------------------------------------------
 // work queue
 // ---------------------------------------------------------------------------
-// Items (head, query block) are split into kXcd contiguous ranges of the
-// head-major item order, balanced by selected-block count (the work), one
-// range per XCD: concurrent workgroups of an XCD then attend to the same
-// head's key/value blocks, which stay resident in that XCD's L2.  Inside a
-// range, items go longest first.  A counting sort on (range, count) writes
-// the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here) is its cursor.
+// A work unit is a (head, query block) item, or one half of its selected-block
+// list when items are split (see split_items below); unit id = 2*item + half.
+// Units are split into kXcd contiguous ranges of the head-major item order,
+// balanced by selected-block count (the work), one range per XCD: concurrent
+// workgroups of an XCD then attend to the same head's key/value blocks, which
+// stay resident in that XCD's L2.  Inside a range, units go head by head and,
+// within a head, longest first: the workgroups of an XCD then stream one
+// head's blocks at a time (mixing heads by length would multiply the blocks
+// in flight per L2).  A counting sort on (range, head group, count) writes
+// the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here) is its cursor;
+// done[item] (zeroed here when split) counts the published halves of an item.
+//
+// Sort bins: along the item order both the range x and the head h are
+// non-decreasing, so x + h numbers the (range, head) pairs in order.  Heads
+// are grouped by 2^hshift and counts by 2^cshift when the bins would not fit
+// in LDS otherwise.
 constexpr int kXcd = 8;
 constexpr int kQueueThreads = 1024;
 constexpr int kQueueMaxBins = kXcd * (4096 + 1);
 
-__device__ __forceinline__ int queue_key(const int32_t* row_ptr, int r, int nkb, int64_t total) {
-  const int c = row_ptr[r + 1] - row_ptr[r];
-  const int64_t mid = (int64_t)row_ptr[r] + c / 2;
-  const int x = total > 0 ? (int)min<int64_t>(kXcd - 1, mid * kXcd / total) : 0;
-  return x * (nkb + 1) + (nkb - min(c, nkb));
+struct QueueShape {
+  int nqb, nkb, hshift, cshift, nc;   // nc = count bins per head group
+};
+
+// Selected-block range [lo, hi) of half `part` of item r (the whole list when
+// the item is not split; halves only for lists of two or more entries).
+struct Range {
+  int lo, hi;
+  bool halved;
+};
+__device__ __forceinline__ Range unit_range(const int32_t* row_ptr, int r, int part, int split) {
+  const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
+  if (!split || e1 - e0 < 2) return {e0, e1, false};
+  const int mid = e0 + (e1 - e0 + 1) / 2;
+  return part ? Range{mid, e1, true} : Range{e0, mid, true};
+}
+
+__device__ __forceinline__ int unit_xcd(Range u, int64_t total) {
+  const int64_t mid = (int64_t)u.lo + (u.hi - u.lo) / 2;
+  return total > 0 ? (int)min<int64_t>(kXcd - 1, mid * kXcd / total) : 0;
+}
+
+__device__ __forceinline__ int queue_key(Range u, int r, const QueueShape& qs, int64_t total) {
+  const int c = min(u.hi - u.lo, qs.nkb);
+  const int pair = unit_xcd(u, total) + ((r / qs.nqb) >> qs.hshift);
+  return pair * qs.nc + ((qs.nkb - c) >> qs.cshift);
 }
 
 __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __restrict__ row_ptr,
-                                                              int rows, int nkb,
-                                                              int32_t* __restrict__ items,
+                                                              int rows, QueueShape qs, int split,
+                                                              int32_t* __restrict__ units,
                                                               int32_t* __restrict__ xq,
-                                                              int32_t* __restrict__ ctr) {
+                                                              int32_t* __restrict__ ctr,
+                                                              int32_t* __restrict__ done) {
   __shared__ int hist[kQueueMaxBins];
+  __shared__ int xcnt[kXcd];
   __shared__ int red[kQueueThreads / kWave + 1];
   const int t = threadIdx.x;
-  const int nb = kXcd * (nkb + 1);
+  const int heads = rows / qs.nqb;
+  const int nb = (kXcd + ((heads - 1) >> qs.hshift) + 1) * qs.nc;
   const int64_t total = row_ptr[rows];
   for (int b = t; b < nb; b += kQueueThreads) hist[b] = 0;
+  if (t < kXcd) xcnt[t] = 0;
+  if (split)
+    for (int r = t; r < rows; r += kQueueThreads) done[r] = 0;
   __syncthreads();
-  for (int r = t; r < rows; r += kQueueThreads) atomicAdd(&hist[queue_key(row_ptr, r, nkb, total)], 1);
+  for (int r = t; r < rows; r += kQueueThreads) {
+    const Range u0 = unit_range(row_ptr, r, 0, split);
+    atomicAdd(&hist[queue_key(u0, r, qs, total)], 1);
+    atomicAdd(&xcnt[unit_xcd(u0, total)], 1);
+    if (u0.halved) {
+      const Range u1 = unit_range(row_ptr, r, 1, split);
+      atomicAdd(&hist[queue_key(u1, r, qs, total)], 1);
+      atomicAdd(&xcnt[unit_xcd(u1, total)], 1);
+    }
+  }
   __syncthreads();
   // exclusive scan of the histogram, contiguous chunk per thread
   const int per = (nb + kQueueThreads - 1) / kQueueThreads;
@@ -80,19 +126,26 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
     hist[b] = run;
     run += c;
   }
-  __syncthreads();
-  if (t < kXcd) {
-    xq[t] = hist[t * (nkb + 1)];
-    ctr[t] = 0;
+  if (t == 0) {
+    int acc = 0;
+    for (int x = 0; x < kXcd; ++x) {
+      xq[x] = acc;
+      ctr[x] = 0;
+      acc += xcnt[x];
+    }
+    xq[kXcd] = acc;
   }
-  if (t == 0) xq[kXcd] = rows;
   __syncthreads();
-  // scatter; the order among items with equal (range, count) is immaterial
-  for (int r = t; r < rows; r += kQueueThreads)
-    items[atomicAdd(&hist[queue_key(row_ptr, r, nkb, total)], 1)] = r;
+  // scatter; the order among units with equal keys is immaterial
+  for (int r = t; r < rows; r += kQueueThreads) {
+    const Range u0 = unit_range(row_ptr, r, 0, split);
+    units[atomicAdd(&hist[queue_key(u0, r, qs, total)], 1)] = 2 * r;
+    if (u0.halved)
+      units[atomicAdd(&hist[queue_key(unit_range(row_ptr, r, 1, split), r, qs, total)], 1)] = 2 * r + 1;
+  }
 }
 
-// Next item for a persistent workgroup: its own XCD's range first, then the
+// Next unit for a persistent workgroup: its own XCD's range first, then the
 // others' (stealing).  -1 when every range is exhausted.
 __device__ __forceinline__ int pop_item(const int32_t* __restrict__ items,
                                         const int32_t* __restrict__ xq, int32_t* ctr, int home) {
@@ -126,7 +179,7 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
   constexpr int SUB = 32;
   __shared__ float4 ks[SUB * D / 4];
   __shared__ float4 vs[SUB * D / 4];
-  const int item = items[blockIdx.x];
+  const int item = items[blockIdx.x] >> 1;   // never split on this path
   const int h = item / nqb, i = item % nqb;
   const int t = threadIdx.x;
   const int64_t a = (int64_t)i * BLK + t;
@@ -205,12 +258,21 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
 //   softmax, PV  O^T += V^T P^T (V from LDS through transposing reads)
 //   barrier      (all waves done with V; the next K has landed)
 //   V loads      the next block's V goes into LDS
+//
+// A halved item (one of two units of its list) ends by publishing its
+// unnormalised partial state, or, when the other half is already published,
+// by combining the two and writing the output (combine_halves).
+constexpr int kPartO = 16 * 256 * 4;              // fp32 O of the 256 lanes
+constexpr int kSlotFloats = kPartO + 2 * 256;     // + running max and sum per lane
+
 __device__ __forceinline__ void attend_item(
-    int item, uint16_t* kl, uint16_t* vl, const uint16_t* __restrict__ q,
+    int unit, int split, float* __restrict__ partial, int32_t* __restrict__ done, int* flag,
+    uint16_t* kl, uint16_t* vl, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ col_slot, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_valid, float scale_log2) {
+  const int item = unit >> 1, part = unit & 1;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
@@ -260,8 +322,9 @@ __device__ __forceinline__ void attend_item(
 
   // every value below is uniform across the workgroup; readfirstlane keeps it
   // in scalar registers (buffer descriptors need them)
-  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[item]);
-  const int e1 = __builtin_amdgcn_readfirstlane(row_ptr[item + 1]);
+  const Range range = unit_range(row_ptr, item, part, split);
+  const int e0 = __builtin_amdgcn_readfirstlane(range.lo);
+  const int e1 = __builtin_amdgcn_readfirstlane(range.hi);
   // source block of entry e (-1: skip)
   auto block_of = [&](int e) -> int64_t {
     const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
@@ -377,6 +440,61 @@ __device__ __forceinline__ void attend_item(
     e = en;
   }
 
+  if (range.halved) {
+    // Partial state of this half, lane-major so that each store instruction
+    // covers 1 KiB: O chunk c = 4u + r4 of lane tid at float4 c*256 + tid.
+    float* mine = partial + ((size_t)item * 2 + part) * kSlotFloats;
+    const float* other = partial + ((size_t)item * 2 + (part ^ 1)) * kSlotFloats;
+    if (tid == 0) *flag = __hip_atomic_load(&done[item], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int merge = *flag;
+    __syncthreads();
+    if (!merge) {
+      // the other half has not published: publish this one (stores, release
+      // fence, then the count); whichever half counts second combines
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          reinterpret_cast<float4*>(mine)[(4 * u + r4) * 256 + tid] =
+              make_float4(oacc[u][4 * r4], oacc[u][4 * r4 + 1], oacc[u][4 * r4 + 2], oacc[u][4 * r4 + 3]);
+      mine[kPartO + tid] = m_run;
+      mine[kPartO + 256 + tid] = l_run;
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) *flag = atomicAdd(&done[item], 1);
+      __syncthreads();
+      merge = *flag;
+      if (!merge) return;
+    }
+    __threadfence();   // acquire: the other half's stores precede its count
+    // Combine in fixed half order (half 0 first), so the result does not
+    // depend on which half finished first: with M = max(m0, m1),
+    //   O = O1 * 2^(m1 - M) + O0 * 2^(m0 - M),  l likewise.
+    const float m_o = other[kPartO + tid], l_o = other[kPartO + 256 + tid];
+    const float m0 = part ? m_o : m_run, m1 = part ? m_run : m_o;
+    const float l0 = part ? l_o : l_run, l1 = part ? l_run : l_o;
+    const float mm = fmaxf(m0, m1);
+    const bool any = mm > -INFINITY;
+    const float a0 = any ? __builtin_amdgcn_exp2f(m0 - mm) : 0.f;
+    const float a1 = any ? __builtin_amdgcn_exp2f(m1 - mm) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 ot = reinterpret_cast<const float4*>(other)[(4 * u + r4) * 256 + tid];
+        const float ov[4] = {ot.x, ot.y, ot.z, ot.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float own = oacc[u][4 * r4 + x];
+          const float v0 = part ? ov[x] : own, v1 = part ? own : ov[x];
+          oacc[u][4 * r4 + x] = fmaf(v1, a1, v0 * a0);
+        }
+      }
+    l_run = fmaf(l1, a1, l0 * a0);
+    m_run = mm;
+  }
+
   // finalise: O[query][d], reg r of d-tile u -> d = 32u + 8(r/4) + 4g + r%4
   const int64_t qrow = (int64_t)i * kB + qloc;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -397,18 +515,19 @@ __device__ __forceinline__ void attend_item(
         live ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
-// Persistent: each workgroup pops items from its XCD's queue until all queues
-// are empty (every workgroup reaches that exit; no workgroup waits on another).
+// Persistent: each workgroup pops units from its XCD's queue until all queues
+// are empty (every workgroup reaches that exit; no workgroup waits on another:
+// the half that combines only reads what the other half already published).
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ col_slot,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     float* __restrict__ lse, const int32_t* __restrict__ items, const int32_t* __restrict__ xq,
-    int32_t* __restrict__ ctr, int nqb, int nkb, int64_t q_rows, int64_t q_valid,
-    int64_t kv_valid, float scale_log2) {
+    int32_t* __restrict__ ctr, int split, float* __restrict__ partial, int32_t* __restrict__ done,
+    int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_valid, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) uint16_t kl[kB * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t vl[kB * kD];
-  __shared__ int next_item;
+  __shared__ int next_item, flag;
   const int home = xcc_id();
   for (;;) {
     if (threadIdx.x == 0) next_item = pop_item(items, xq, ctr, home);
@@ -416,8 +535,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const int item = __builtin_amdgcn_readfirstlane(next_item);   // uniform: scalar loads below
     __syncthreads();
     if (item < 0) break;
-    attend_item(item, kl, vl, q, row_ptr, col_idx, col_slot, k, v, out, lse, nqb, nkb, q_rows,
-                q_valid, kv_valid, scale_log2);
+    attend_item(item, split, partial, done, &flag, kl, vl, q, row_ptr, col_idx, col_slot, k, v, out,
+                lse, nqb, nkb, q_rows, q_valid, kv_valid, scale_log2);
   }
 }
 
@@ -435,15 +554,6 @@ hipError_t f32_launch(const Dims& g, const void* q, const int32_t* row_ptr,
 
 }  // namespace
 
-hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s) {
-  const int rows = g.H * g.nqb;
-  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, s, row_ptr, rows, g.nkb, items,
-                     items + rows, items + rows + kXcd + 1);
-  return hipGetLastError();
-}
-
-int queue_words(int rows) { return rows + 2 * kXcd + 1; }
-
 namespace {
 int cu_count() {
   static int cached[64] = {0};
@@ -457,6 +567,33 @@ int cu_count() {
   }
   return cached[dev];
 }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+// units (up to two per item), xq, ctr, done
+size_t queue_bytes(int rows) { return round256(sizeof(int32_t) * ((size_t)3 * rows + 2 * kXcd + 1)); }
+size_t partial_bytes(int rows) { return sizeof(float) * (size_t)rows * 2 * kSlotFloats; }
+
+// Items are split in halves when whole items would leave the last round of
+// the persistent grid (two workgroups per CU) more than 5% idle: items of
+// near-equal length then finish together, one round short of the whole
+// grid.  Halving doubles the rounds and so halves that idle fraction.
+bool split_items(const Dims& g) {
+  if (g.dtype != SA_BF16) return false;
+  const int64_t rows = (int64_t)g.H * g.nqb, slots = 2 * (int64_t)cu_count();
+  const int64_t rounds = (rows + slots - 1) / slots;
+  return (double)(rounds * slots) > 1.05 * (double)rows;
+}
+
+
+// Finest head grouping, then count resolution, whose sort bins fit in LDS.
+QueueShape queue_shape(const Dims& g) {
+  for (int hs = 0; hs < 31; ++hs)
+    for (int cs = 0; cs <= 13; ++cs) {
+      const int64_t nc = (g.nkb >> cs) + 1, groups = ((int64_t)(g.H - 1) >> hs) + 1;
+      if ((kXcd + groups) * nc <= kQueueMaxBins) return {g.nqb, g.nkb, hs, cs, (int)nc};
+    }
+  return {g.nqb, g.nkb, 31, 13, 1};
+}
 }  // namespace
 
 bool attn_supported(int dtype, int d, int B) {
@@ -464,25 +601,43 @@ bool attn_supported(int dtype, int d, int B) {
   return (d == 64 || d == 128) && (B == 64 || B == 128);
 }
 
+size_t attn_ws_bytes(const Dims& g) {
+  const int rows = g.H * g.nqb;
+  return queue_bytes(rows) + (split_items(g) ? partial_bytes(rows) : 0);
+}
+
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
-                       const void* v, void* out, float* lse, int32_t* items,
+                       const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
                        float sm_scale, hipStream_t s) {
   const int rows = g.H * g.nqb;
+  int32_t* units = static_cast<int32_t*>(ws);
+  int32_t* xq = units + 2 * rows;
+  int32_t* ctr = xq + kXcd + 1;
+  int32_t* done = ctr + kXcd;
+  // halves only when the workspace holds their partial states (it was sized
+  // on this device by attn_ws_bytes)
+  const int split = split_items(g) && ws_bytes >= queue_bytes(rows) + partial_bytes(rows);
+  float* partial = split ? reinterpret_cast<float*>(static_cast<char*>(ws) + queue_bytes(rows)) : nullptr;
+  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, s, row_ptr, rows,
+                     queue_shape(g), split, units, xq, ctr, done);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (g.dtype == SA_BF16) {
     if (g.d != kD || g.B != kB) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    const int grid = std::min(rows, 2 * cu_count());   // two resident workgroups per CU
+    // two resident workgroups per CU, no more than there are units
+    const int grid = std::min((split ? 2 : 1) * rows, 2 * cu_count());
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)q,
                        row_ptr, col_idx, col_slot, (const uint16_t*)k, (const uint16_t*)v,
-                       (uint16_t*)out, lse, items, items + rows, items + rows + kXcd + 1, g.nqb,
-                       g.nkb, g.q_rows, g.q_valid, g.kv_valid, scale_log2);
+                       (uint16_t*)out, lse, units, xq, ctr, split, partial, done, g.nqb, g.nkb,
+                       g.q_rows, g.q_valid, g.kv_valid, scale_log2);
     return hipGetLastError();
   }
-  if (g.d == 64 && g.B == 64) return f32_launch<64, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, items, sm_scale, s);
-  if (g.d == 64 && g.B == 128) return f32_launch<64, 128>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, items, sm_scale, s);
-  if (g.d == 128 && g.B == 64) return f32_launch<128, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, items, sm_scale, s);
-  if (g.d == 128 && g.B == 128) return f32_launch<128, 128>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, items, sm_scale, s);
+  if (g.d == 64 && g.B == 64) return f32_launch<64, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, units, sm_scale, s);
+  if (g.d == 64 && g.B == 128) return f32_launch<64, 128>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, units, sm_scale, s);
+  if (g.d == 128 && g.B == 64) return f32_launch<128, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, units, sm_scale, s);
+  if (g.d == 128 && g.B == 128) return f32_launch<128, 128>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, units, sm_scale, s);
   return hipErrorInvalidValue;
 }
 

@@ -114,10 +114,12 @@ hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* 
                        const void* k, const void* v, void* kp, void* vp, int64_t cap,
                        const int32_t* row_ptr, const int32_t* col_idx, const int32_t* slot_of,
                        int32_t* col_slot, hipStream_t s);
-hipError_t launch_queue(const Dims& g, const int32_t* row_ptr, int32_t* items, hipStream_t s);
+// Work queue (longest first, per-XCD ranges) and attention in one call; ws
+// holds attn_ws_bytes(g) bytes sized on the current device.
+size_t attn_ws_bytes(const Dims& g);
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
-                       const void* v, void* out, float* lse, int32_t* items,
+                       const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
                        float sm_scale, hipStream_t s);
 hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int64_t q_start,
                               int64_t q_valid, int32_t* order, int32_t* inverse, int32_t* q_order,

@@ -173,7 +173,13 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr,
  * col_slot == NULL: k_src, v_src are the full K, V [H,kv_rows,d].
  * col_slot != NULL: k_src, v_src are packed [slots,B,d] and entry e reads
  *                   slot col_slot[e] (col_idx still gives the block id).
- * Work items (head, query block) are processed longest-first.
+ * Work items (head, query block) are processed head by head, longest first
+ * within a head.  When whole items would leave the device's last round of
+ * work more than 5% idle, each item's block list is processed as two halves
+ * whose partial results are combined in a fixed order, so results never
+ * depend on timing; the workspace then also holds the halves' partial
+ * states (66 KiB per item), and its size depends on the CU count of the
+ * device that is current when sa_workspace_size is called.
  * out: [H,q_rows,d] input dtype; lse_opt: NULL or fp32 [H,q_rows]. */
 int sparse_attn_forward(const sa_problem* prob, const void* q,
                         const int32_t* row_ptr, const int32_t* col_idx,
