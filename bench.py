@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--unpacked", action="store_true", help="attend straight from K/V (no pack)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the untimed load-balance and dense-context measurements")
     ap.add_argument("--cpu-items", type=int, default=256,
                     help="(head, query block) items in the oracle's timed sample")
     ap.add_argument("--tiles", default=None, metavar="TT,TH,TW",
@@ -267,9 +269,79 @@ def main():
             "tflops": round(bflops / (bms / 1e3) / 1e12, 3),
             "frac_of_peak": round(bflops / (bms / 1e3) / 1e12 / peak, 4),
             "flops_counted": "10*B^2*d per selected pair (five GEMMs; recomputed S and dP not counted)"}
+    if w.dtype == "bf16" and not args.no_extras:
+        rec["load_balance"] = load_balance(sa, packed, flush, fwd_ms)
+        rec["dense_context"] = dense_context(w, d, sa, flush, fwd_ms, flops)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items)
     print(json.dumps(rec), flush=True)
+
+
+def _flush(flush, k=0):
+    if flush is not None:
+        flush[0].fill_(k & 0xff)
+        flush[1].amax()
+
+
+def _timed(fn, flush, reps):
+    """Median ms of `reps` runs of fn, each after a cache flush."""
+    import numpy as np
+    import torch
+    ts = []
+    for r in range(reps):
+        _flush(flush, r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def load_balance(sa, packed, flush, fwd_ms, reps=3):
+    """Busy time of each persistent workgroup (device clock stamps at its
+    start and when it finds no more work): max / mean over workgroups, the
+    single-GPU reading of the load imbalance the Top-p abstract reports
+    across ranks.  Beside it, the same forward launched one workgroup per
+    work unit (hardware dispatch, no queue kernel reuse of workgroups)."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_scores_amd import binding
+    n = sa.workgroups(binding.SA_SCHEDULE_PERSISTENT)
+    clk = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    imb, span = [], []
+    for r in range(reps):
+        _flush(flush, r)
+        sa.forward(packed=packed, wg_clock=clk)
+        torch.cuda.synchronize()
+        c = clk.view(n, 2).cpu().numpy().astype(np.float64)
+        busy = c[:, 1] - c[:, 0]
+        imb.append(busy.max() / busy.mean())
+        span.append((c[:, 1].max() - c[:, 0].min()) / busy.mean())
+    per_unit = _timed(lambda: sa.forward(packed=packed, schedule=binding.SA_SCHEDULE_PER_UNIT),
+                      flush, reps)
+    return {"workgroups": n, "busy_max_over_mean": round(float(np.median(imb)), 4),
+            "span_over_mean_busy": round(float(np.median(span)), 4),
+            "persistent_forward_ms": round(fwd_ms, 4),
+            "per_unit_workgroups": sa.workgroups(binding.SA_SCHEDULE_PER_UNIT),
+            "per_unit_forward_ms": round(per_unit, 4), "reps": reps}
+
+
+def dense_context(w, d, sa, flush, fwd_ms, flops, reps=3):
+    """The same attention kernel with every block selected (p = 1), attending
+    straight from K/V: what the sparse forward is measured against."""
+    from block_sparse_attention_scores_amd.path import SparseAttention
+    dn = SparseAttention(w.with_(top_p=1.0, select_mode=0), sa.q, sa.k, sa.v, d.get("wq"),
+                         d.get("wk"), packed_cap=1)
+    dn.select()
+    dense_pairs = w.heads * w.n_qb * w.n_kb
+    assert dn.nnz() == dense_pairs
+    ms = _timed(lambda: dn.forward(packed=False), flush, reps)
+    dflops = flops / sa.nnz() * dense_pairs
+    del dn
+    return {"forward_ms": round(ms, 4), "tflops": round(dflops / (ms / 1e3) / 1e12, 3),
+            "sparse_forward_speedup": round(ms / fwd_ms, 3), "reps": reps}
 
 
 if __name__ == "__main__":

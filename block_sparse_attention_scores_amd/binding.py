@@ -27,10 +27,12 @@ SA_F32, SA_BF16 = 0, 1
 SA_TOP_P, SA_TOP_K = 0, 1
 SA_SCORE_POOLED, SA_SCORE_LOWRANK, SA_SCORE_LOWRANK_MAX = 0, 1, 2
 SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD, SA_STAGE_BACKWARD = 0, 1, 2, 3, 4
+SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT = 0, 1
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-           "kv_demand_pack", "sparse_attn_forward", "sparse_attn_backward",
-           "sa_video_block_order", "sa_permute_rows", "sa_status_string", "sa_abi_version")
+           "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
+           "sparse_attn_forward_ex", "sparse_attn_backward", "sa_video_block_order",
+           "sa_permute_rows", "sa_status_string", "sa_abi_version")
 
 
 class SaProblem(ctypes.Structure):
@@ -51,6 +53,11 @@ class SaProblem(ctypes.Structure):
         ("score_mode", ctypes.c_int32),
         ("rank", ctypes.c_int32),
     ]
+
+
+class SaForwardOpts(ctypes.Structure):
+    _fields_ = [("schedule", ctypes.c_int32), ("clock_cap", ctypes.c_int32),
+                ("wg_clock", ctypes.c_void_p)]
 
 
 class SaVideoTiling(ctypes.Structure):
@@ -86,6 +93,9 @@ def load(path: str = None):
     lib.sparse_attn_csr_from_mask.argtypes = [prob, P, P, P, P, sz, P]
     lib.kv_demand_pack.argtypes = [prob, P, P, P, P, P, P, P, P, P, i64, P, P, sz, P]
     lib.sparse_attn_forward.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.sa_forward_workgroups.argtypes = [prob, i32, ctypes.POINTER(i32)]
+    lib.sparse_attn_forward_ex.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz,
+                                           ctypes.POINTER(SaForwardOpts), P]
     lib.sparse_attn_backward.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.sa_video_block_order.argtypes = [ctypes.POINTER(SaVideoTiling), i64, i64, P, P, P, P, P]
     lib.sa_permute_rows.argtypes = [i32, i64, i32, P, P, i64, P, i64, P]
@@ -93,8 +103,9 @@ def load(path: str = None):
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_abi_version.argtypes = []
     for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
-                 "kv_demand_pack", "sparse_attn_forward", "sparse_attn_backward",
-                 "sa_video_block_order", "sa_permute_rows", "sa_abi_version"):
+                 "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
+                 "sparse_attn_forward_ex", "sparse_attn_backward", "sa_video_block_order",
+                 "sa_permute_rows", "sa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -164,6 +175,27 @@ def sparse_attn_forward(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, 
     _check("sparse_attn_forward", load().sparse_attn_forward(
         ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
         _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sa_forward_workgroups(prob: SaProblem, schedule: int) -> int:
+    n = ctypes.c_int32(0)
+    _check("sa_forward_workgroups",
+           load().sa_forward_workgroups(ctypes.byref(prob), schedule, ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
+                           ws_bytes, schedule=SA_SCHEDULE_PERSISTENT, wg_clock=None,
+                           clock_cap=0, stream=None):
+    """``wg_clock``: None or an int64 device tensor of at least 2 * clock_cap
+    entries (clock_cap defaults to its length / 2)."""
+    if wg_clock is not None and not clock_cap:
+        clock_cap = wg_clock.numel() // 2
+    opts = SaForwardOpts(schedule, clock_cap, _ptr(wg_clock))
+    _check("sparse_attn_forward_ex", load().sparse_attn_forward_ex(
+        ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
+        _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, ctypes.byref(opts),
+        _stream(stream)))
 
 
 def sparse_attn_backward(prob, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv, ws,

@@ -145,7 +145,7 @@ T* at(void* ws, size_t off) {
 
 extern "C" {
 
-int sa_abi_version(void) { return 3; }
+int sa_abi_version(void) { return 4; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -248,10 +248,21 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr, const int32_t
   return SA_OK;
 }
 
-int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* row_ptr,
-                        const int32_t* col_idx, const int32_t* col_slot, const void* k_src,
-                        const void* v_src, void* out, float* lse_opt, void* ws, size_t ws_bytes,
-                        void* stream) {
+int sa_forward_workgroups(const sa_problem* prob, int32_t schedule, int32_t* workgroups) {
+  Dims g;
+  const int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (!workgroups) return SA_ERR_INVALID_ARG;
+  if (schedule != SA_SCHEDULE_PERSISTENT && schedule != SA_SCHEDULE_PER_UNIT) return SA_ERR_INVALID_ARG;
+  if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
+  *workgroups = sa::attn_workgroups(g, schedule);
+  return SA_OK;
+}
+
+int sparse_attn_forward_ex(const sa_problem* prob, const void* q, const int32_t* row_ptr,
+                           const int32_t* col_idx, const int32_t* col_slot, const void* k_src,
+                           const void* v_src, void* out, float* lse_opt, void* ws,
+                           size_t ws_bytes, const sa_forward_opts* opts, void* stream) {
   Dims g;
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
@@ -260,13 +271,33 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
   if (!aligned16(q) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(out))
     return SA_ERR_INVALID_ARG;
   if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  int schedule = SA_SCHEDULE_PERSISTENT;
+  uint64_t* wg_clock = nullptr;
+  if (opts) {
+    schedule = opts->schedule;
+    if (schedule != SA_SCHEDULE_PERSISTENT && schedule != SA_SCHEDULE_PER_UNIT)
+      return SA_ERR_INVALID_ARG;
+    if (opts->wg_clock && g.dtype == SA_BF16) {
+      if (((uintptr_t)opts->wg_clock & 7u) || opts->clock_cap < sa::attn_workgroups(g, schedule))
+        return SA_ERR_INVALID_ARG;
+      wg_clock = opts->wg_clock;
+    }
+  }
   st = check_ws(g, SA_STAGE_FORWARD, ws, ws_bytes);
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
   SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
-                             ws_bytes, sm, s));
+                             ws_bytes, sm, schedule, wg_clock, s));
   return SA_OK;
+}
+
+int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* row_ptr,
+                        const int32_t* col_idx, const int32_t* col_slot, const void* k_src,
+                        const void* v_src, void* out, float* lse_opt, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt,
+                                ws, ws_bytes, nullptr, stream);
 }
 
 int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, const void* v,

@@ -22,6 +22,7 @@
 //                online softmax in the exp2 domain; P^T goes straight from the
 //                accumulator registers into the B operand of O^T = V^T P^T.
 #include <float.h>
+#include <limits.h>
 #include <math.h>
 
 #include <algorithm>
@@ -515,8 +516,10 @@ __device__ __forceinline__ void attend_item(
         live ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
-// Persistent: each workgroup pops units from its XCD's queue until all queues
-// are empty (every workgroup reaches that exit; no workgroup waits on another:
+// Persistent (max_units unbounded): each workgroup pops units from its XCD's
+// queue until all queues are empty; with max_units = 1 and one workgroup per
+// unit it is the plain one-item-per-workgroup launch.  Either way every
+// workgroup exits once the queues are empty (every workgroup reaches that exit; no workgroup waits on another:
 // the half that combines only reads what the other half already published).
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ row_ptr,
@@ -524,12 +527,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
     float* __restrict__ lse, const int32_t* __restrict__ items, const int32_t* __restrict__ xq,
     int32_t* __restrict__ ctr, int split, float* __restrict__ partial, int32_t* __restrict__ done,
-    int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_valid, float scale_log2) {
+    int max_units, uint64_t* __restrict__ wg_clock, int nqb, int nkb, int64_t q_rows,
+    int64_t q_valid, int64_t kv_valid, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) uint16_t kl[kB * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t vl[kB * kD];
   __shared__ int next_item, flag;
+  const uint64_t t_start = wg_clock ? __builtin_amdgcn_s_memrealtime() : 0;
   const int home = xcc_id();
-  for (;;) {
+  for (int n = 0; n < max_units; ++n) {
     if (threadIdx.x == 0) next_item = pop_item(items, xq, ctr, home);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(next_item);   // uniform: scalar loads below
@@ -537,6 +542,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     if (item < 0) break;
     attend_item(item, split, partial, done, &flag, kl, vl, q, row_ptr, col_idx, col_slot, k, v, out,
                 lse, nqb, nkb, q_rows, q_valid, kv_valid, scale_log2);
+  }
+  if (wg_clock && threadIdx.x == 0) {
+    wg_clock[2 * blockIdx.x] = t_start;
+    wg_clock[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
@@ -606,10 +615,17 @@ size_t attn_ws_bytes(const Dims& g) {
   return queue_bytes(rows) + (split_items(g) ? partial_bytes(rows) : 0);
 }
 
+int attn_workgroups(const Dims& g, int schedule) {
+  const int rows = g.H * g.nqb;
+  if (g.dtype != SA_BF16) return rows;
+  const int units = (split_items(g) ? 2 : 1) * rows;
+  return schedule == SA_SCHEDULE_PER_UNIT ? units : std::min(units, 2 * cu_count());
+}
+
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
                        const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
-                       float sm_scale, hipStream_t s) {
+                       float sm_scale, int schedule, uint64_t* wg_clock, hipStream_t s) {
   const int rows = g.H * g.nqb;
   int32_t* units = static_cast<int32_t*>(ws);
   int32_t* xq = units + 2 * rows;
@@ -626,12 +642,15 @@ hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
   if (g.dtype == SA_BF16) {
     if (g.d != kD || g.B != kB) return hipErrorInvalidValue;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    // two resident workgroups per CU, no more than there are units
-    const int grid = std::min((split ? 2 : 1) * rows, 2 * cu_count());
+    // persistent: two resident workgroups per CU, no more than there are units
+    const int nunits = (split ? 2 : 1) * rows;
+    const bool per_unit = schedule == SA_SCHEDULE_PER_UNIT;
+    const int grid = per_unit ? nunits : std::min(nunits, 2 * cu_count());
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)q,
                        row_ptr, col_idx, col_slot, (const uint16_t*)k, (const uint16_t*)v,
-                       (uint16_t*)out, lse, units, xq, ctr, split, partial, done, g.nqb, g.nkb,
-                       g.q_rows, g.q_valid, g.kv_valid, scale_log2);
+                       (uint16_t*)out, lse, units, xq, ctr, split, partial, done,
+                       per_unit ? 1 : INT_MAX, wg_clock, g.nqb, g.nkb, g.q_rows, g.q_valid,
+                       g.kv_valid, scale_log2);
     return hipGetLastError();
   }
   if (g.d == 64 && g.B == 64) return f32_launch<64, 64>(g, q, row_ptr, col_idx, col_slot, k, v, out, lse, units, sm_scale, s);

@@ -117,10 +117,11 @@ hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* 
 // Work queue (longest first, per-XCD ranges) and attention in one call; ws
 // holds attn_ws_bytes(g) bytes sized on the current device.
 size_t attn_ws_bytes(const Dims& g);
+int attn_workgroups(const Dims& g, int schedule);
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
                        const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
-                       float sm_scale, hipStream_t s);
+                       float sm_scale, int schedule, uint64_t* wg_clock, hipStream_t s);
 hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int64_t q_start,
                               int64_t q_valid, int32_t* order, int32_t* inverse, int32_t* q_order,
                               int32_t* q_inverse, hipStream_t s);

@@ -84,15 +84,23 @@ class SparseAttention:
                          self.demand_idx, self.col_slot, self.k_packed, self.v_packed,
                          self.packed_cap, self.dev_status, ws, n)
 
-    def forward(self, packed: bool = True, lse: bool = True):
+    def forward(self, packed: bool = True, lse: bool = True, schedule=None, wg_clock=None):
+        """Attention over the selected blocks.  ``schedule`` (an
+        SA_SCHEDULE_* value) or ``wg_clock`` (int64 device tensor, two stamps
+        per workgroup) route the call through sparse_attn_forward_ex."""
         ws, n = self._ws(B.SA_STAGE_FORWARD)
-        if packed:
-            B.sparse_attn_forward(self.prob, self.q, self.row_ptr, self.col_idx, self.col_slot,
-                                  self.k_packed, self.v_packed, self.out,
-                                  self.lse if lse else None, ws, n)
+        src = ((self.col_slot, self.k_packed, self.v_packed) if packed
+               else (None, self.k, self.v))
+        args = (self.prob, self.q, self.row_ptr, self.col_idx) + src + (
+            self.out, self.lse if lse else None, ws, n)
+        if schedule is None and wg_clock is None:
+            B.sparse_attn_forward(*args)
         else:
-            B.sparse_attn_forward(self.prob, self.q, self.row_ptr, self.col_idx, None, self.k,
-                                  self.v, self.out, self.lse if lse else None, ws, n)
+            B.sparse_attn_forward_ex(*args, schedule=B.SA_SCHEDULE_PERSISTENT
+                                     if schedule is None else schedule, wg_clock=wg_clock)
+
+    def workgroups(self, schedule=B.SA_SCHEDULE_PERSISTENT) -> int:
+        return B.sa_forward_workgroups(self.prob, schedule)
 
     def run(self, packed: bool = True):
         self.select()

@@ -187,6 +187,45 @@ int sparse_attn_forward(const sa_problem* prob, const void* q,
                         const void* v_src, void* out, float* lse_opt, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Work schedules of the attention forward (sparse_attn_forward_ex). */
+typedef enum sa_schedule {
+  SA_SCHEDULE_PERSISTENT = 0, /* what sparse_attn_forward runs: two workgroups
+                                 per CU take work units from per-XCD queues
+                                 until all are done                           */
+  SA_SCHEDULE_PER_UNIT = 1    /* one workgroup per work unit, handed out by the
+                                 hardware dispatcher (the plain launch, kept as
+                                 a measured alternative)                      */
+} sa_schedule;
+
+/* Options of sparse_attn_forward_ex (host struct, read synchronously). */
+typedef struct sa_forward_opts {
+  int32_t schedule;    /* sa_schedule                                          */
+  int32_t clock_cap;   /* capacity of wg_clock, in workgroups                  */
+  uint64_t* wg_clock;  /* NULL, or device [clock_cap, 2]: for each workgroup of
+                          the bf16 attention launch, the device's constant-rate
+                          clock (s_memrealtime ticks) when it started and when
+                          it found no more work                               */
+} sa_forward_opts;
+
+/* Workgroups of the bf16 attention launch under `schedule` for this problem
+ * on the current device (an upper bound on the units for SA_SCHEDULE_PER_UNIT,
+ * whose surplus workgroups exit at once).  workgroups: host pointer. */
+int sa_forward_workgroups(const sa_problem* prob, int32_t schedule, int32_t* workgroups);
+
+/* sparse_attn_forward with a chosen work schedule and optional per-workgroup
+ * clock stamps, the measurement behind the load-imbalance figure (max over
+ * mean of the workgroups' busy time) that the Top-p sparse-attention
+ * abstract reports for its rank-level stragglers.  Results are bit-identical
+ * to sparse_attn_forward's under either schedule.  The fp32 path always runs
+ * one workgroup per item and writes no clock stamps.  SA_ERR_INVALID_ARG for
+ * an unknown schedule, or a wg_clock with clock_cap below
+ * sa_forward_workgroups.  opts == NULL is sparse_attn_forward. */
+int sparse_attn_forward_ex(const sa_problem* prob, const void* q,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const int32_t* col_slot, const void* k_src,
+                           const void* v_src, void* out, float* lse_opt, void* ws,
+                           size_t ws_bytes, const sa_forward_opts* opts, void* stream);
+
 /* Gradients of sparse_attn_forward for an upstream gradient dout (the
  * training workload: the DSV explainer's speedups, "What it costs", are
  * training numbers).  With P = softmax(z) of the forward (same selected
@@ -255,8 +294,9 @@ int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 3 (1, plus the video block order entry points
- * in 2, plus sparse_attn_backward in 3). */
+/* ABI version of this header: 4 (1, plus the video block order entry points
+ * in 2, plus sparse_attn_backward in 3, plus sparse_attn_forward_ex and
+ * sa_forward_workgroups in 4). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

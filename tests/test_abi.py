@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 3
+    assert lib.sa_abi_version() == 4
 
 
 def test_struct_layout_matches_c():
@@ -214,3 +214,48 @@ def test_backward_validation(lib):
     bad[0] = FAKE + 8                     # q not 16-byte aligned
     assert call(prob, bad) == B.SA_ERR_INVALID_ARG
     assert call(prob, args, need - 1) == B.SA_ERR_WORKSPACE
+
+
+def test_forward_ex_validation(lib):
+    p = good_problem()
+    _, n = status_of_ws(p, B.SA_STAGE_FORWARD)
+    wg = ctypes.c_int32(0)
+    assert lib.sa_forward_workgroups(ctypes.byref(p), B.SA_SCHEDULE_PERSISTENT, ctypes.byref(wg)) == 0
+    persist = wg.value
+    assert lib.sa_forward_workgroups(ctypes.byref(p), B.SA_SCHEDULE_PER_UNIT, ctypes.byref(wg)) == 0
+    per_unit = wg.value
+    assert 0 < persist <= per_unit
+    assert lib.sa_forward_workgroups(ctypes.byref(p), 2, ctypes.byref(wg)) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_forward_workgroups(ctypes.byref(p), 0, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_forward_workgroups(None, 0, ctypes.byref(wg)) == B.SA_ERR_INVALID_ARG
+
+    f = lib.sparse_attn_forward_ex
+    base = [ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE * 4, n]
+
+    def call(opts, args=base):
+        return f(*args, ctypes.byref(opts), None)
+
+    assert call(B.SaForwardOpts(2, 0, None)) == B.SA_ERR_INVALID_ARG          # unknown schedule
+    assert call(B.SaForwardOpts(-1, 0, None)) == B.SA_ERR_INVALID_ARG
+    assert call(B.SaForwardOpts(B.SA_SCHEDULE_PERSISTENT, persist - 1, FAKE)) == B.SA_ERR_INVALID_ARG
+    assert call(B.SaForwardOpts(B.SA_SCHEDULE_PER_UNIT, per_unit - 1, FAKE)) == B.SA_ERR_INVALID_ARG
+    assert call(B.SaForwardOpts(B.SA_SCHEDULE_PERSISTENT, persist, FAKE + 4)) == B.SA_ERR_INVALID_ARG
+    bad = list(base); bad[7] = None
+    assert call(B.SaForwardOpts(0, 0, None), bad) == B.SA_ERR_INVALID_ARG    # no output
+    bad = list(base); bad[10] = 0
+    assert call(B.SaForwardOpts(0, 0, None), bad) == B.SA_ERR_WORKSPACE
+
+
+def test_forward_workgroups_at_480p_geometry(lib):
+    # 12 heads x 256 query blocks = 3072 items: whole items (six full rounds
+    # of a 512-workgroup persistent grid on 256 CUs, the count also assumed
+    # when no device is visible)
+    p = good_problem(heads=12, q_rows=32768, q_valid=32760, kv_rows=32768, kv_valid=32760)
+    assert B.sa_forward_workgroups(p, B.SA_SCHEDULE_PERSISTENT) == 512
+    assert B.sa_forward_workgroups(p, B.SA_SCHEDULE_PER_UNIT) == 3072
+    # 24 x 117 = 2808 items would leave the sixth round half idle: halved
+    p = good_problem(heads=24, q_rows=14976, q_valid=14864, kv_rows=118912, kv_valid=118800)
+    assert B.sa_forward_workgroups(p, B.SA_SCHEDULE_PERSISTENT) == 512
+    assert B.sa_forward_workgroups(p, B.SA_SCHEDULE_PER_UNIT) == 2 * 2808
+    f32 = good_problem(dtype=B.SA_F32)
+    assert B.sa_forward_workgroups(f32, B.SA_SCHEDULE_PERSISTENT) == 2 * 4

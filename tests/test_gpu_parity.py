@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from oracle import oracle as O
+from block_sparse_attention_scores_amd import binding as B
 from block_sparse_attention_scores_amd import inputs as I
 from block_sparse_attention_scores_amd.path import SparseAttention, to_device
 
@@ -348,4 +349,29 @@ def test_whole_items_when_rows_fill_the_grid():
     w = small_bf16(name="whole", heads=8, latent=(8, 32, 32), q_valid=8192, top_p=0.6,
                    top_k=2, seed=42)
     assert w.heads * w.n_qb == 512
-    full_check(w)
+    sa, _, _ = full_check(w)
+    check_schedules(sa)
+
+
+def check_schedules(sa):
+    """Both work schedules give the persistent result bit for bit; every
+    workgroup stamps a start and an end."""
+    o1, l1 = sa.out.clone(), sa.lse.clone()
+    for sched in (B.SA_SCHEDULE_PER_UNIT, B.SA_SCHEDULE_PERSISTENT):
+        n = sa.workgroups(sched)
+        clk = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+        sa.out.zero_()
+        sa.lse.zero_()
+        sa.forward(schedule=sched, wg_clock=clk)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, sa.out) and torch.equal(l1, sa.lse), sched
+        c = clk.view(n, 2).cpu()
+        assert bool((c[:, 0] > 0).all()) and bool((c[:, 1] >= c[:, 0]).all())
+        say(f"  schedule {sched}: {n} workgroups, busy max/mean "
+            f"{float((c[:, 1] - c[:, 0]).max()) / float((c[:, 1] - c[:, 0]).double().mean()):.3f}")
+
+
+def test_schedules_agree_on_halved_items():
+    w = small_bf16(name="sched", seed=43)
+    sa, x = run_path(w)
+    check_schedules(sa)
