@@ -46,6 +46,7 @@ SELECT_TOP_K = 1
 SCORE_POOLED = 0
 SCORE_LOWRANK = 1
 SCORE_LOWRANK_MAX = 2   # token-level predicted scores, max over the block pair
+SCORE_LOWRANK_MASS = 3  # token-level predicted scores, predicted softmax mass of the block pair
 
 
 @dataclasses.dataclass(frozen=True)
@@ -161,8 +162,16 @@ def lowrank_max() -> Workload:
                                score_mode=SCORE_LOWRANK_MAX)
 
 
+def lowrank_mass() -> Workload:
+    """The low-rank workload with token-level predicted scores aggregated by
+    the predicted softmax mass of each block pair (temperature 1/sqrt(d))."""
+    return dataclasses.replace(lowrank(), name="lowrank_tokenmass_128k",
+                               score_mode=SCORE_LOWRANK_MASS)
+
+
 NAMED = {"tiny": tiny, "480p": c480p, "720p_rank": c720p_rank,
-         "lowrank": lowrank, "hetero": hetero, "lowrank_max": lowrank_max}
+         "lowrank": lowrank, "hetero": hetero, "lowrank_max": lowrank_max,
+         "lowrank_mass": lowrank_mass}
 
 
 def named(name: str) -> Workload:

@@ -132,6 +132,48 @@ def block_scores_lowrank_max(q: np.ndarray, k: np.ndarray, q_valid: int, kv_vali
     return s
 
 
+def block_scores_lowrank_mass(q: np.ndarray, k: np.ndarray, q_valid: int, kv_valid: int,
+                              block: int, wq: np.ndarray, wk: np.ndarray, scale: float,
+                              items: Optional[Sequence[tuple]] = None) -> np.ndarray:
+    """Token-level variant of the rank-r predictor aggregated by predicted
+    attention mass, fp64.
+
+    The DSV explainer ("The idea") predicts query-key scores token by token
+    with two small low-rank matrices in place of the full scores.  Reading
+    the predicted scores as attention logits at temperature `scale`, each
+    valid query a of query block i spreads a predicted softmax over all valid
+    keys; the block pair's mass is the mean over those queries of what key
+    block j receives:
+
+        z_ab = scale * (q_a W_q) . (k_b W_k)
+        M[i, j] = (1 / n_i) * sum_{a in i} sum_{b in j} exp(z_ab) / sum_b' exp(z_ab')
+
+    The score is S = ln M, so that a softmax over the row (top-p) gives back
+    the masses (each row of M sums to one) and top-k keeps the largest
+    masses.  q [H, q_rows, d], k [H, kv_rows, d], wq, wk [H, d, r].  items:
+    optional (h, i) rows to compute (others are left NaN).  Returns
+    [H, nQB, nKB].
+    """
+    H = q.shape[0]
+    nqb, nkb = q.shape[1] // block, k.shape[1] // block
+    s = np.full((H, nqb, nkb), np.nan)
+    todo = [(h, i) for h in range(H) for i in range(nqb)] if items is None else items
+    kt = {}
+    for h, i in todo:
+        if h not in kt:
+            kt[h] = np.matmul(k[h, :kv_valid].astype(np.float64), wk[h].astype(np.float64))
+        lo, hi = i * block, min((i + 1) * block, q_valid)
+        qt = np.matmul(q[h, lo:hi].astype(np.float64), wq[h].astype(np.float64))
+        z = scale * np.matmul(qt, kt[h].T)               # [tokens of block i, kv_valid]
+        z -= z.max(axis=1, keepdims=True)
+        p = np.exp(z)
+        p /= p.sum(axis=1, keepdims=True)                # predicted softmax of each query
+        for j in range(nkb):
+            m = p[:, j * block:min((j + 1) * block, kv_valid)].sum(axis=1).mean()
+            s[h, i, j] = math.log(m) if m > 0.0 else -math.inf
+    return s
+
+
 # ---------------------------------------------------------------------------
 # A4/A5: selection
 # ---------------------------------------------------------------------------
@@ -496,8 +538,10 @@ def scores_for(q, k, q_valid, kv_valid, block, score_mode, score_scale, wq=None,
         s = block_scores_pooled(qbar, kbar, score_scale)
     elif score_mode == 1:
         s = block_scores_lowrank(qbar, kbar, wq, wk)
-    else:
+    elif score_mode == 2:
         s = block_scores_lowrank_max(q, k, q_valid, kv_valid, block, wq, wk)
+    else:
+        s = block_scores_lowrank_mass(q, k, q_valid, kv_valid, block, wq, wk, score_scale)
     return qbar, kbar, s
 
 

@@ -739,3 +739,77 @@ def test_lowrank_max_bounds_the_mean():
     rows = O.block_scores_lowrank_max(q, k, 60, 90, B, wq, wk, items=[(1, 2)])
     np.testing.assert_array_equal(rows[1, 2], smax[1, 2])
     assert np.isnan(rows[0, 0]).all()
+
+
+# ---------------------------------------------------------------------------
+# token-level low-rank predictor, aggregation by predicted softmax mass
+# ---------------------------------------------------------------------------
+def _mass_inputs(seed, H=2, B=4, d=3, r=2, q_rows=12, kv_rows=16, qv=10, kv=13):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((H, q_rows, d)).astype(np.float32)
+    k = g.standard_normal((H, kv_rows, d)).astype(np.float32)
+    q[:, qv:] = 0; k[:, kv:] = 0
+    wq = g.standard_normal((H, d, r)).astype(np.float32)
+    wk = g.standard_normal((H, d, r)).astype(np.float32)
+    return q, k, wq, wk, qv, kv
+
+
+def test_lowrank_mass_by_token_pair_loops():
+    q, k, wq, wk, qv, kv = _mass_inputs(60)
+    H, B, d, r, scale = 2, 4, 3, 2, 0.7
+    s = O.block_scores_lowrank_mass(q, k, qv, kv, B, wq, wk, scale)
+    for h in range(H):
+        def proj(x, w, t):
+            return [sum(float(x[h, t, e]) * float(w[h, e, c]) for e in range(d)) for c in range(r)]
+        kt = [proj(k, wk, b) for b in range(kv)]
+        for i in range(3):
+            rows = range(i * B, min((i + 1) * B, qv))
+            mass = [0.0] * 4
+            for a in rows:
+                qa = proj(q, wq, a)
+                z = [scale * sum(qa[c] * kt[b][c] for c in range(r)) for b in range(kv)]
+                den = sum(math.exp(v) for v in z)
+                for b in range(kv):
+                    mass[b // B] += math.exp(z[b]) / den / len(rows)
+            for j in range(4):
+                assert abs(s[h, i, j] - math.log(mass[j])) <= 1e-12
+
+
+def test_lowrank_mass_rows_sum_to_one_and_items():
+    q, k, wq, wk, qv, kv = _mass_inputs(61, H=3, B=8, d=16, r=4, q_rows=40, kv_rows=56,
+                                        qv=37, kv=50)
+    s = O.block_scores_lowrank_mass(q, k, qv, kv, 8, wq, wk, 0.25)
+    np.testing.assert_allclose(np.exp(s).sum(axis=2), 1.0, atol=1e-12)
+    rows = O.block_scores_lowrank_mass(q, k, qv, kv, 8, wq, wk, 0.25, items=[(2, 4), (0, 1)])
+    np.testing.assert_array_equal(rows[2, 4], s[2, 4])
+    np.testing.assert_array_equal(rows[0, 1], s[0, 1])
+    assert np.isnan(rows[1, 0]).all()
+
+
+def test_lowrank_mass_zero_predictor_is_key_share():
+    # W = 0: every predicted logit is 0, each query spreads its mass evenly
+    # over the valid keys, so block j gets (valid keys of j) / kv_valid
+    q, k, wq, wk, qv, kv = _mass_inputs(62, B=8, d=4, r=2, q_rows=24, kv_rows=40, qv=19, kv=35)
+    s = O.block_scores_lowrank_mass(q, k, qv, kv, 8, wq * 0, wk * 0, 1.0)
+    want = np.log(np.array([8, 8, 8, 8, 3]) / 35.0)
+    for h in range(2):
+        for i in range(3):
+            np.testing.assert_allclose(s[h, i], want, atol=1e-14)
+
+
+def test_lowrank_mass_identity_predictor_is_exact_block_mass():
+    # r = d and W = I: the predicted logits are the attention logits, so the
+    # block masses are the true ones (computed token by token in
+    # exact_block_mass with its own softmax)
+    g = np.random.default_rng(63)
+    H, B, d = 2, 8, 6
+    q = g.standard_normal((H, 32, d)).astype(np.float32)
+    k = g.standard_normal((H, 48, d)).astype(np.float32)
+    q[:, 29:] = 0; k[:, 45:] = 0
+    eye = np.stack([np.eye(d, dtype=np.float32)] * H)
+    sc = 1.0 / math.sqrt(d)
+    s = O.block_scores_lowrank_mass(q, k, 29, 45, B, eye, eye, sc)
+    for h in range(H):
+        for i in range(4):
+            m = O.exact_block_mass(q, k, 29, 45, B, sc, h, i)
+            np.testing.assert_allclose(np.exp(s[h, i]), m, rtol=1e-12, atol=1e-15)
