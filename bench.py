@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="480p", help="tiny | 480p | 720p_rank | lowrank | hetero")
+    ap.add_argument("--config", default="480p",
+                    help="tiny | 480p | 720p_rank | lowrank | hetero | lowrank_max | lowrank_mass")
     ap.add_argument("--unpacked", action="store_true", help="attend straight from K/V (no pack)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -89,32 +90,50 @@ def cpu_baseline(w, x, n_items):
     from threadpoolctl import threadpool_info
     from oracle import oracle as O
 
+    rows = w.heads * w.n_qb
+    # token-level scores cost a pass over every token pair of a row: score
+    # and select the sampled rows only (CSR, demand and pack then cover
+    # them), and sample fewer rows so the leg stays near 15 s
+    token = w.score_mode in (2, 3)
+    n_items = min(n_items // 4 if token else n_items, rows)
+    pick = np.random.default_rng(0).choice(rows, size=n_items, replace=False)
+    items = [(int(r) // w.n_qb, int(r) % w.n_qb) for r in sorted(pick)]
     t0 = time.perf_counter()
-    _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
-                           w.eff_score_scale, x.get("wq"), x.get("wk"))
-    mask, _ = O.select(s, w.select_mode, w.top_p, w.top_k)
+    if token:
+        if w.score_mode == 2:
+            s = O.block_scores_lowrank_max(x["q"], x["k"], w.q_valid, w.kv_valid, w.block,
+                                           x["wq"], x["wk"], items=items)
+        else:
+            s = O.block_scores_lowrank_mass(x["q"], x["k"], w.q_valid, w.kv_valid, w.block,
+                                            x["wq"], x["wk"], w.eff_score_scale, items=items)
+        mask = np.zeros(s.shape, bool)
+        for h, i in items:
+            rec = (O.select_row_top_p(s[h, i], w.top_p, w.top_k) if w.select_mode == 0
+                   else O.select_row_top_k(s[h, i], w.top_k))
+            mask[h, i, rec.order[:rec.m]] = True
+    else:
+        _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
+                               w.eff_score_scale, x.get("wq"), x.get("wk"))
+        mask, _ = O.select(s, w.select_mode, w.top_p, w.top_k)
     rp, ci = O.csr(mask)
     dp, di, _, _ = O.demand(mask, rp, ci)
     O.pack(x["k"], dp, di, w.block)
     O.pack(x["v"], dp, di, w.block)
     t_sel = time.perf_counter() - t0
-    rows = w.heads * w.n_qb
-    n_items = min(n_items, rows)
-    pick = np.random.default_rng(0).choice(rows, size=n_items, replace=False)
-    items = [(int(r) // w.n_qb, int(r) % w.n_qb) for r in sorted(pick)]
+    sel_rows = n_items if token else rows
     t0 = time.perf_counter()
     O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block, w.eff_sm_scale,
                 items=items)
     t_att = time.perf_counter() - t0
     nnz_sample = int(sum(mask[h, i].sum() for h, i in items))
-    t = t_att + t_sel * n_items / rows
+    t = t_att + t_sel * n_items / sel_rows
     flops = 4.0 * w.block * w.block * w.head_dim * nnz_sample
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"{n_items} of {rows} (head, query-block) items of {w.name}: dense fp32 "
                        f"masked attention for the sample ({t_att:.2f} s) + fp64 selection, CSR, "
-                       f"demand and pack of all rows ({t_sel:.2f} s) pro-rated by "
-                       f"{n_items}/{rows}"),
+                       f"demand and pack of " + ("the sampled rows" if token else "all rows") +
+                       f" ({t_sel:.2f} s) pro-rated by {n_items}/{sel_rows}"),
             "seconds": round(t_att + t_sel, 3), "host_cpus": os.cpu_count()}
 
 
@@ -237,7 +256,8 @@ def main():
                    "block": w.block, "q_tokens": w.q_valid, "kv_tokens": w.kv_valid,
                    "latent_thw": list(w.latent), "top_p": w.top_p, "top_k": w.top_k,
                    "select_mode": "top_p" if w.select_mode == 0 else "top_k",
-                   "score": ("pooled", f"lowrank{w.rank}", f"lowrank{w.rank}_tokenmax")[w.score_mode],
+                   "score": ("pooled", f"lowrank{w.rank}", f"lowrank{w.rank}_tokenmax",
+                             f"lowrank{w.rank}_tokenmass")[w.score_mode],
                    "packed_kv": packed, "cache": "warm" if flush is None else "flushed each step",
                    "layout": "tiles " + "x".join(map(str, tiles)) if tiles else "raster"},
         "ms_per_layer": round(ms_step, 4),

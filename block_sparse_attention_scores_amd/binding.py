@@ -25,7 +25,7 @@ SA_ERR_CAPACITY = -5
 
 SA_F32, SA_BF16 = 0, 1
 SA_TOP_P, SA_TOP_K = 0, 1
-SA_SCORE_POOLED, SA_SCORE_LOWRANK, SA_SCORE_LOWRANK_MAX = 0, 1, 2
+SA_SCORE_POOLED, SA_SCORE_LOWRANK, SA_SCORE_LOWRANK_MAX, SA_SCORE_LOWRANK_MASS = 0, 1, 2, 3
 SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD, SA_STAGE_BACKWARD = 0, 1, 2, 3, 4
 SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT = 0, 1
 

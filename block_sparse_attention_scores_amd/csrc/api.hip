@@ -44,10 +44,12 @@ int check_problem(const sa_problem* p, Dims* g) {
   if (p->select_mode == SA_TOP_P && p->top_k < 0) return SA_ERR_INVALID_ARG;
   if (p->select_mode == SA_TOP_K && p->top_k < 1) return SA_ERR_INVALID_ARG;
   if (p->score_mode != SA_SCORE_POOLED && p->score_mode != SA_SCORE_LOWRANK &&
-      p->score_mode != SA_SCORE_LOWRANK_MAX)
+      p->score_mode != SA_SCORE_LOWRANK_MAX && p->score_mode != SA_SCORE_LOWRANK_MASS)
     return SA_ERR_INVALID_ARG;
   if (p->score_mode != SA_SCORE_POOLED && (p->rank < 1 || p->rank > 64)) return SA_ERR_INVALID_ARG;
-  if (p->score_mode == SA_SCORE_LOWRANK_MAX && p->rank != 16) return SA_ERR_UNSUPPORTED;
+  if ((p->score_mode == SA_SCORE_LOWRANK_MAX || p->score_mode == SA_SCORE_LOWRANK_MASS) &&
+      p->rank != 16)
+    return SA_ERR_UNSUPPORTED;
   if (!isfinite(p->sm_scale) || !isfinite(p->score_scale)) return SA_ERR_INVALID_ARG;
   g->H = p->num_heads;
   g->d = p->head_dim;
@@ -67,7 +69,7 @@ int check_problem(const sa_problem* p, Dims* g) {
 
 // Workspace layout of every stage, in carve order.
 struct SelectWs {
-  size_t qbar, kbar, qt, kt, qtok, ktok, scores, counts, total;
+  size_t qbar, kbar, qt, kt, qtok, ktok, lse, scores, counts, total;
 };
 SelectWs select_ws(const Dims& g) {
   SelectWs w{};
@@ -76,9 +78,13 @@ SelectWs select_ws(const Dims& g) {
   w.kbar = o; o += round_up(sizeof(double) * g.H * g.nkb * g.d);
   w.qt = o; o += round_up(sizeof(double) * g.H * g.nqb * g.rank);
   w.kt = o; o += round_up(sizeof(double) * g.H * g.nkb * g.rank);
-  const size_t tok = g.score_mode == SA_SCORE_LOWRANK_MAX ? 16 : 0;   // projected tokens
+  const bool token = g.score_mode == SA_SCORE_LOWRANK_MAX || g.score_mode == SA_SCORE_LOWRANK_MASS;
+  const size_t tok = token ? 16 : 0;   // projected tokens
   w.qtok = o; o += round_up(sizeof(float) * g.H * g.q_rows * tok);
   w.ktok = o; o += round_up(sizeof(float) * g.H * g.kv_rows * tok);
+  // per query token and key block: ln of the predicted exp-sum (mass mode)
+  const size_t lse_n = g.score_mode == SA_SCORE_LOWRANK_MASS ? (size_t)g.H * g.nkb * g.q_rows : 0;
+  w.lse = o; o += round_up(sizeof(float) * lse_n);
   w.scores = o; o += round_up(sizeof(double) * g.H * g.nqb * g.nkb);
   w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nqb);
   w.total = o;
@@ -196,6 +202,10 @@ int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, con
   if (g.score_mode == SA_SCORE_LOWRANK_MAX) {
     SA_TRY_HIP(sa::launch_lowrank_max(g, q, k, wq, wk, at<float>(ws, w.qtok),
                                       at<float>(ws, w.ktok), scores, s));
+  } else if (g.score_mode == SA_SCORE_LOWRANK_MASS) {
+    const float tau = prob->score_scale > 0.f ? prob->score_scale : (float)(1.0 / sqrt((double)g.d));
+    SA_TRY_HIP(sa::launch_lowrank_mass(g, q, k, wq, wk, tau, at<float>(ws, w.qtok),
+                                       at<float>(ws, w.ktok), at<float>(ws, w.lse), scores, s));
   } else if (g.rank > 0) {
     SA_TRY_HIP(sa::launch_scores(g, qt, kt, g.rank, 1.0, scores, s));
   } else {

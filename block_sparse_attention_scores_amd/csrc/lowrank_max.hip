@@ -106,9 +106,8 @@ hipError_t project(const T* x, const float* w, int H, int64_t rows, int64_t vali
 
 }  // namespace
 
-hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const float* wq,
-                              const float* wk, float* qtok, float* ktok, double* scores,
-                              hipStream_t s) {
+hipError_t launch_token_projection(const Dims& g, const void* q, const void* k, const float* wq,
+                                   const float* wk, float* qtok, float* ktok, hipStream_t s) {
   hipError_t e;
   if (g.dtype == SA_BF16) {
     e = project((const uint16_t*)q, wq, g.H, g.q_rows, g.q_valid, g.d, g.B, qtok, s);
@@ -117,6 +116,13 @@ hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const
     e = project((const float*)q, wq, g.H, g.q_rows, g.q_valid, g.d, g.B, qtok, s);
     if (e == hipSuccess) e = project((const float*)k, wk, g.H, g.kv_rows, g.kv_valid, g.d, g.B, ktok, s);
   }
+  return e;
+}
+
+hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const float* wq,
+                              const float* wk, float* qtok, float* ktok, double* scores,
+                              hipStream_t s) {
+  const hipError_t e = launch_token_projection(g, q, k, wq, wk, qtok, ktok, s);
   if (e != hipSuccess) return e;
   const dim3 grid((g.nkb + kRunKB - 1) / kRunKB, g.nqb, g.H);
   hipLaunchKernelGGL(blockmax_kernel, grid, dim3(256), 0, s, qtok, ktok, g.nqb, g.nkb, g.B,

@@ -133,6 +133,11 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
                            void* dv, float* delta, uint32_t* bits, int32_t* counts,
                            int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s);
+hipError_t launch_token_projection(const Dims& g, const void* q, const void* k, const float* wq,
+                                   const float* wk, float* qtok, float* ktok, hipStream_t s);
+hipError_t launch_lowrank_mass(const Dims& g, const void* q, const void* k, const float* wq,
+                               const float* wk, float tau, float* qtok, float* ktok, float* lbuf,
+                               double* scores, hipStream_t s);
 hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const float* wq,
                               const float* wk, float* qtok, float* ktok, double* scores,
                               hipStream_t s);

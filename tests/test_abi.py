@@ -92,7 +92,8 @@ def test_workspace_sizes(lib):
     (dict(score_mode=B.SA_SCORE_LOWRANK, rank=65), B.SA_ERR_INVALID_ARG),
     (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=8), B.SA_ERR_UNSUPPORTED),
     (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=0), B.SA_ERR_INVALID_ARG),
-    (dict(score_mode=3), B.SA_ERR_INVALID_ARG),
+    (dict(score_mode=B.SA_SCORE_LOWRANK_MASS, rank=32), B.SA_ERR_UNSUPPORTED),
+    (dict(score_mode=4), B.SA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), B.SA_ERR_INVALID_ARG),
 ])
 def test_problem_validation(lib, kw, expect):
@@ -121,6 +122,13 @@ def test_select_argument_errors(lib):
     lm = good_problem(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=16)
     bad = list(args); bad[0] = ctypes.byref(lm)
     assert f(*bad) == B.SA_ERR_INVALID_ARG                     # token max without W
+    ms = good_problem(score_mode=B.SA_SCORE_LOWRANK_MASS, rank=16)
+    bad = list(args); bad[0] = ctypes.byref(ms)
+    assert f(*bad) == B.SA_ERR_INVALID_ARG                     # token mass without W
+    # the mass mode keeps ln sum exp per query token and key block: 4*H*nKB*q_rows bytes more
+    st_m, n_m = status_of_ws(ms)
+    st_x, n_x = status_of_ws(lm)
+    assert st_m == st_x == 0 and n_m - n_x >= 4 * 2 * 8 * 512
 
 
 def test_pack_and_forward_argument_errors(lib):

@@ -136,3 +136,51 @@ def test_full_size_token_max_sampled_rows():
                 for h, i in items]
         say(f"  {tag:9s} scores: recall of true mass on {len(items)} rows mean {np.mean(vals):.4f} "
             f"min {np.min(vals):.4f}")
+
+
+def test_full_size_token_mass_sampled_rows():
+    """The low-rank workload with predicted-mass scores at full size: the
+    selection of sampled rows against the oracle (its predicted softmax for
+    those rows' queries only), then CSR on every row and attention on
+    sampled items, all from the GPU's mask."""
+    from test_gpu_parity import tokenmass_rel
+    w = I.named("lowrank_mass")
+    say("workload", w.name)
+    x = I.generate(w)
+    d = to_device(x, w)
+    sa = SparseAttention(w, d["q"], d["k"], d["v"], d["wq"], d["wk"])
+    sa.run(packed=True)
+    torch.cuda.synchronize()
+    assert int(sa.dev_status.item()) == 0
+    mask = O.bits_to_mask(sa.mask_bits.cpu().numpy().view(np.uint32), w.heads, w.n_qb, w.n_kb)
+    assert np.all(mask.sum(axis=2) == w.top_k)
+    rows = sampled_items(w, np.concatenate([[0], np.cumsum(mask.sum(axis=2).ravel())]), n_random=6)
+    s = O.block_scores_lowrank_mass(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, x["wq"],
+                                    x["wk"], w.eff_score_scale, items=rows)
+    rel = tokenmass_rel(w, x, np.nan_to_num(s, nan=1.0))
+    excused = 0
+    for h, i in rows:
+        rec = O.select_row_top_k(s[h, i], w.top_k)
+        want = np.zeros(w.n_kb, bool)
+        want[rec.order[:rec.m]] = True
+        if not np.array_equal(want, mask[h, i]):
+            assert O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, mask[h, i],
+                                          rel=max(1e-6, float(rel[h, i]))), (h, i)
+            excused += 1
+    rp, ci = sa.host_csr()
+    orp, oci = O.csr(mask)
+    np.testing.assert_array_equal(rp, orp)
+    np.testing.assert_array_equal(ci, oci)
+    items = sampled_items(w, orp, n_random=2)
+    o, lse = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
+                         w.eff_sm_scale, items=items)
+    go = sa.out.float().cpu().numpy()
+    for h, i in items:
+        sl = slice(i * w.block, (i + 1) * w.block)
+        assert float(np.max(np.abs(go[h, sl] - o[h, sl]))) <= TOL_OUT[w.dtype]
+    say(f"  {len(rows)} sampled rows checked, near-tie rows excused: {excused}")
+    vals = [float((O.exact_block_mass(x["q"], x["k"], w.q_valid, w.kv_valid, w.block,
+                                      w.eff_sm_scale, h, i) * mask[h, i]).sum())
+            for h, i in items]
+    say(f"  token mass scores: recall of true mass on {len(items)} rows mean {np.mean(vals):.4f} "
+        f"min {np.min(vals):.4f}")

@@ -63,7 +63,8 @@ def check_selection(w, sa, x, rows_to_check=None):
     if nkb % 32:
         assert np.all(bits[:, -1] >> np.uint32(nkb % 32) == 0)
     excused = 0
-    rel = tokenmax_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MAX else None
+    rel = (tokenmax_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MAX else
+           tokenmass_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MASS else None)
     for h in range(w.heads):
         for i in range(w.n_qb):
             if w.select_mode == I.SELECT_TOP_P:
@@ -101,6 +102,31 @@ def tokenmax_rel(w, x, s):
             rel[:, i] = delta / np.abs(s[:, i]).max(axis=1)
         else:
             rel[:, i] = 2 * delta
+    return rel
+
+
+def tokenmass_rel(w, x, s):
+    """Near-tie tolerance of the predicted-mass scores, per row.  A logit
+    tau * q~.k~ is within tau * delta of the exact one (delta as in
+    tokenmax_rel: fp32 projections and fp32 16-term products); the fp32
+    exponentials, logarithms and sums add at most about 64 * 2^-24 to the
+    log-masses.  So ln M (the score S) is within eps = 2 (tau delta + 2^-18)
+    of the exact one, i.e. M is within relative eps.  Top-k compares S
+    (relative to the row's max |S|), top-p the masses (relative, 2 eps for
+    margin)."""
+    qt = np.matmul(x["q"][:, :w.q_valid].astype(np.float64), x["wq"].astype(np.float64))
+    kt = np.matmul(x["k"][:, :w.kv_valid].astype(np.float64), x["wk"].astype(np.float64))
+    qn = np.linalg.norm(qt, axis=2)
+    kn = np.linalg.norm(kt, axis=2).max(axis=1)                          # [H]
+    tau = w.eff_score_scale
+    rel = np.zeros((w.heads, w.n_qb))
+    for i in range(w.n_qb):
+        lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
+        eps = 2.0 * (tau * 2.0 ** -19 * qn[:, lo:hi].max(axis=1) * kn + 2.0 ** -18)
+        if w.select_mode == I.SELECT_TOP_K:
+            rel[:, i] = eps / np.abs(s[:, i]).max(axis=1)
+        else:
+            rel[:, i] = 2 * eps
     return rel
 
 
@@ -218,6 +244,26 @@ def test_lowrank_token_max(mode, p, k):
     sa, _, mask = full_check(w)
     if mode == I.SELECT_TOP_K:
         assert np.all(mask.sum(axis=2) == min(k, w.n_kb))
+
+
+@pytest.mark.parametrize("mode,p,k", [(I.SELECT_TOP_K, 0.9, 5), (I.SELECT_TOP_P, 0.5, 2)])
+def test_lowrank_token_mass(mode, p, k):
+    """Token-level rank-16 predicted scores, aggregated by predicted softmax
+    mass (several key tiles, a ragged last key block and query block)."""
+    w = small_bf16(name="tokmass", heads=2, latent=(4, 16, 37), q_valid=700,
+                   select_mode=mode, top_p=p, top_k=k, score_mode=I.SCORE_LOWRANK_MASS,
+                   score_scale=0.5, seed=73)
+    sa, _, mask = full_check(w)
+    if mode == I.SELECT_TOP_K:
+        assert np.all(mask.sum(axis=2) == min(k, w.n_kb))
+
+
+def test_f32_token_mass_block_64():
+    w = I.Workload("tokmass_f32", heads=2, head_dim=64, block=64, dtype="f32", latent=(3, 10, 20),
+                   q_start=0, q_valid=450, seed=74, strength=1.0, tile=(1, 4, 4), clusters=4,
+                   select_mode=I.SELECT_TOP_P, top_p=0.6, top_k=2,
+                   score_mode=I.SCORE_LOWRANK_MASS)
+    full_check(w)
 
 
 def test_f32_token_max_block_64():
