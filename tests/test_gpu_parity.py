@@ -421,3 +421,18 @@ def test_schedules_agree_on_halved_items():
     w = small_bf16(name="sched", seed=43)
     sa, x = run_path(w)
     check_schedules(sa)
+
+
+def test_max_key_blocks_single_query_one_key_tail():
+    """4096 key blocks (the largest count the library takes), the last of
+    which holds one valid key, against a single valid query: the LDS sort
+    past 1024 blocks, block lists of a few hundred entries in halves, and a
+    work queue whose count bins are coarsened to fit LDS."""
+    w = small_bf16(name="max_nkb", heads=2, latent=(1, 1, 4095 * 128 + 1), q_valid=1,
+                   tile=(1, 1, 512), clusters=8, top_p=0.5, top_k=4, seed=44)
+    assert w.n_kb == 4096 and w.kv_valid % w.block == 1 and w.n_qb == 1
+    sa, _, mask = full_check(w)
+    lens = mask.sum(axis=2)
+    say(f"  list lengths {lens.min()}..{lens.max()}")
+    assert lens.min() >= 4
+    check_schedules(sa)
