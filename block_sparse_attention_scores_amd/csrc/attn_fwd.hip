@@ -42,12 +42,14 @@ using namespace bf16mma;
 // Units are split into kXcd contiguous ranges of the head-major item order,
 // balanced by selected-block count (the work), one range per XCD: concurrent
 // workgroups of an XCD then attend to the same head's key/value blocks, which
-// stay resident in that XCD's L2.  Inside a range, units go head by head and,
-// within a head, longest first: the workgroups of an XCD then stream one
-// head's blocks at a time (mixing heads by length would multiply the blocks
-// in flight per L2).  A counting sort on (range, head group, count) writes
-// the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here) is its cursor;
-// done[item] (zeroed here when split) counts the published halves of an item.
+// stay resident in that XCD's L2.  Inside a range, units go head by head,
+// first halves before second halves, and longest first within those: the
+// workgroups of an XCD then stream one range of one head's blocks at a time
+// (mixing heads by length, or the two halves of a head, would multiply the
+// blocks in flight per L2).  A counting sort on (range, head group, half,
+// count) writes the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here)
+// is its cursor; done[item] (zeroed here when split) counts the published
+// halves of an item.
 //
 // Sort bins: along the item order both the range x and the head h are
 // non-decreasing, so x + h numbers the (range, head) pairs in order.  Heads
@@ -79,10 +81,11 @@ __device__ __forceinline__ int unit_xcd(Range u, int64_t total) {
   return total > 0 ? (int)min<int64_t>(kXcd - 1, mid * kXcd / total) : 0;
 }
 
-__device__ __forceinline__ int queue_key(Range u, int r, const QueueShape& qs, int64_t total) {
+__device__ __forceinline__ int queue_key(Range u, int r, int part, const QueueShape& qs,
+                                         int64_t total) {
   const int c = min(u.hi - u.lo, qs.nkb);
   const int pair = unit_xcd(u, total) + ((r / qs.nqb) >> qs.hshift);
-  return pair * qs.nc + ((qs.nkb - c) >> qs.cshift);
+  return (2 * pair + part) * qs.nc + ((qs.nkb - c) >> qs.cshift);
 }
 
 __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __restrict__ row_ptr,
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
   __shared__ int red[kQueueThreads / kWave + 1];
   const int t = threadIdx.x;
   const int heads = rows / qs.nqb;
-  const int nb = (kXcd + ((heads - 1) >> qs.hshift) + 1) * qs.nc;
+  const int nb = 2 * (kXcd + ((heads - 1) >> qs.hshift) + 1) * qs.nc;
   const int64_t total = row_ptr[rows];
   for (int b = t; b < nb; b += kQueueThreads) hist[b] = 0;
   if (t < kXcd) xcnt[t] = 0;
@@ -105,11 +108,11 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
   __syncthreads();
   for (int r = t; r < rows; r += kQueueThreads) {
     const Range u0 = unit_range(row_ptr, r, 0, split);
-    atomicAdd(&hist[queue_key(u0, r, qs, total)], 1);
+    atomicAdd(&hist[queue_key(u0, r, 0, qs, total)], 1);
     atomicAdd(&xcnt[unit_xcd(u0, total)], 1);
     if (u0.halved) {
       const Range u1 = unit_range(row_ptr, r, 1, split);
-      atomicAdd(&hist[queue_key(u1, r, qs, total)], 1);
+      atomicAdd(&hist[queue_key(u1, r, 1, qs, total)], 1);
       atomicAdd(&xcnt[unit_xcd(u1, total)], 1);
     }
   }
@@ -140,9 +143,10 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
   // scatter; the order among units with equal keys is immaterial
   for (int r = t; r < rows; r += kQueueThreads) {
     const Range u0 = unit_range(row_ptr, r, 0, split);
-    units[atomicAdd(&hist[queue_key(u0, r, qs, total)], 1)] = 2 * r;
+    units[atomicAdd(&hist[queue_key(u0, r, 0, qs, total)], 1)] = 2 * r;
     if (u0.halved)
-      units[atomicAdd(&hist[queue_key(unit_range(row_ptr, r, 1, split), r, qs, total)], 1)] = 2 * r + 1;
+      units[atomicAdd(&hist[queue_key(unit_range(row_ptr, r, 1, split), r, 1, qs, total)], 1)] =
+          2 * r + 1;
   }
 }
 
@@ -599,7 +603,7 @@ QueueShape queue_shape(const Dims& g) {
   for (int hs = 0; hs < 31; ++hs)
     for (int cs = 0; cs <= 13; ++cs) {
       const int64_t nc = (g.nkb >> cs) + 1, groups = ((int64_t)(g.H - 1) >> hs) + 1;
-      if ((kXcd + groups) * nc <= kQueueMaxBins) return {g.nqb, g.nkb, hs, cs, (int)nc};
+      if (2 * (kXcd + groups) * nc <= kQueueMaxBins) return {g.nqb, g.nkb, hs, cs, (int)nc};
     }
   return {g.nqb, g.nkb, 31, 13, 1};
 }
