@@ -13,11 +13,13 @@
 // so that a softmax over a row of S gives back the masses (each row of M sums
 // to one) and top-k keeps the largest masses.
 //
-//   (projections: launch_token_projection, fp64 sums stored as fp32)
+//   (projections: launch_token_projection, fp64 sums rounded to fp32 and
+//    stored as bf16 hi + lo)
 //   block_lse_kernel   one workgroup per (head, query block, run of key
 //                      blocks); each wave forms S^T = K~ Q~^T for its 32 query
-//                      tokens against a key block on v_mfma_f32_32x32x2_f32
-//                      (keys as rows, so each lane holds one query's scores),
+//                      tokens against a key block (split-bf16 matrix-core
+//                      products, token_mma.h; keys as rows, so each lane
+//                      holds one query's scores),
 //                      masks keys past kv_valid, and writes L[a, j] (fp32,
 //                      layout [H, nKB, q_rows]: 32 consecutive queries per
 //                      store).
@@ -30,19 +32,19 @@
 
 #include <algorithm>
 
-#include "sa_common.h"
+#include "token_mma.h"
 
 namespace sa {
 namespace {
 
-constexpr int kTokRank = 16;
+constexpr int kTokWords = 32;   // bf16 hi and lo of the 16 components per token
 constexpr int kRunKB = 16;      // key blocks per workgroup in block_lse_kernel
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int B>
-__global__ __launch_bounds__(256) void block_lse_kernel(const float* __restrict__ qt,
-                                                        const float* __restrict__ kt, int nkb,
+__global__ __launch_bounds__(256, 2) void block_lse_kernel(const uint16_t* __restrict__ qt,
+                                                        const uint16_t* __restrict__ kt, int nkb,
                                                         int64_t q_rows, int64_t kv_rows,
                                                         int64_t kv_valid, float tau,
                                                         float* __restrict__ L) {
@@ -52,47 +54,45 @@ __global__ __launch_bounds__(256) void block_lse_kernel(const float* __restrict_
   if (wave >= kTiles) return;   // B = 64: two waves hold the block's queries
   const int jn = min(kRunKB, nkb - j0);
   const int64_t qrow = (int64_t)i * B + 32 * wave + lr;
-  // B operand: this lane's query, rank index 8g + s at step s
-  const float4* qa = reinterpret_cast<const float4*>(qt + ((int64_t)h * q_rows + qrow) * kTokRank + 8 * g);
-  const float4 b0 = qa[0], b1 = qa[1];
-  const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-  const float tl = tau * kLog2e;   // logits in log2 units
+  // B operand: this lane's query, rank components 8g .. 8g+7
+  const token::Split bq = token::split_load(qt + ((int64_t)h * q_rows + qrow) * kTokWords, g);
+  const float tl = tau * kLog2e;   // logits in log2 units: z * log2(e) = tl * score
   for (int jj = 0; jj < jn; ++jj) {
     const int j = j0 + jj;
     const int64_t key0 = (int64_t)j * B;
     // valid keys of this block (uniform); only the last block is ragged
     const int lim = (int)min<int64_t>(B, kv_valid - key0);
-    float x[kTiles][16];
-    float mx = -INFINITY;
+    f32x16 acc[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      const float4* kp = reinterpret_cast<const float4*>(
-          kt + ((int64_t)h * kv_rows + key0 + 32 * t + lr) * kTokRank + 8 * g);
-      const float4 a0 = kp[0], a1 = kp[1];
-      const float ak[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      f32x16 acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ak[s], bq[s], acc, 0, 0, 0);
-      // reg r: key 32t + 8(r/4) + 4g + r%4 of the block, this lane's query
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = key < lim ? acc[r] * tl : -INFINITY;
-        x[t][r] = v;
-        mx = fmaxf(mx, v);
-      }
+      const token::Split ak =
+          token::split_load(kt + ((int64_t)h * kv_rows + key0 + 32 * t + lr) * kTokWords, g);
+      acc[t] = token::scores(ak, bq);
     }
+    // reg r of tile t: key 32t + 8(r/4) + 4g + r%4 of the block, this lane's query
+    if (__builtin_expect(lim < B, 0)) {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) acc[t][r] = -INFINITY;
+    }
+    // max of the raw scores (tl > 0), then exp2(tl * s - tl * max) as one FMA
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float off = -mx * tl;
     float sum = 0.f;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(x[t][r] - mx);
+      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][r], tl, off));
     sum += __shfl_xor(sum, 32, kWave);
     // every block holds a valid key, so mx is finite and sum >= 1
-    if (g == 0) L[((int64_t)h * nkb + j) * q_rows + qrow] = (mx + __log2f(sum)) * kLn2;
+    if (g == 0) L[((int64_t)h * nkb + j) * q_rows + qrow] = (mx * tl + __log2f(sum)) * kLn2;
   }
 }
 
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const float* __restrict
 }  // namespace
 
 hipError_t launch_lowrank_mass(const Dims& g, const void* q, const void* k, const float* wq,
-                               const float* wk, float tau, float* qtok, float* ktok, float* lbuf,
-                               double* scores, hipStream_t s) {
+                               const float* wk, float tau, uint16_t* qtok, uint16_t* ktok,
+                               float* lbuf, double* scores, hipStream_t s) {
   hipError_t e = launch_token_projection(g, q, k, wq, wk, qtok, ktok, s);
   if (e != hipSuccess) return e;
   const dim3 grid((g.nkb + kRunKB - 1) / kRunKB, g.nqb, g.H);

@@ -84,12 +84,12 @@ def check_selection(w, sa, x, rows_to_check=None):
 
 def tokenmax_rel(w, x, s):
     """Near-tie tolerance of the token-level max scores, per row.  The GPU
-    rounds the projected tokens to fp32 and forms each 16-term dot product in
-    fp32: its error is at most about 18 * 2^-24 * sum_c |q~_c k~_c| <= 2^-19 *
-    |q~_a| |k~_b| (doubled for margin), so a block score is within
-    delta = 2^-19 max_a |q~_a| max_b |k~_b| of the exact one.  Top-k compares
-    scores (relative to the row's max |S|), top-p softmax masses (relative
-    error up to 2 delta)."""
+    rounds the projected tokens to fp32, splits each into bf16 hi + lo and
+    sums hi.hi + hi.lo + lo.hi in fp32: a 16-term dot product is within about
+    2^-16 sum_c |q~_c k~_c| <= 2^-16 |q~_a| |k~_b| of the exact one (doubled
+    for margin), so a block score is within delta = 2^-15 max_a |q~_a|
+    max_b |k~_b|.  Top-k compares scores (relative to the row's max |S|),
+    top-p softmax masses (relative error up to 2 delta)."""
     qt = np.matmul(x["q"][:, :w.q_valid].astype(np.float64), x["wq"].astype(np.float64))
     kt = np.matmul(x["k"][:, :w.kv_valid].astype(np.float64), x["wk"].astype(np.float64))
     qn = np.linalg.norm(qt, axis=2)
@@ -97,7 +97,7 @@ def tokenmax_rel(w, x, s):
     rel = np.zeros((w.heads, w.n_qb))
     for i in range(w.n_qb):
         lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
-        delta = 2.0 ** -19 * qn[:, lo:hi].max(axis=1) * kn
+        delta = 2.0 ** -15 * qn[:, lo:hi].max(axis=1) * kn
         if w.select_mode == I.SELECT_TOP_K:
             rel[:, i] = delta / np.abs(s[:, i]).max(axis=1)
         else:
@@ -108,7 +108,7 @@ def tokenmax_rel(w, x, s):
 def tokenmass_rel(w, x, s):
     """Near-tie tolerance of the predicted-mass scores, per row.  A logit
     tau * q~.k~ is within tau * delta of the exact one (delta as in
-    tokenmax_rel: fp32 projections and fp32 16-term products); the fp32
+    tokenmax_rel: split-bf16 products of the fp32 projections); the fp32
     exponentials, logarithms and sums add at most about 64 * 2^-24 to the
     log-masses.  So ln M (the score S) is within eps = 2 (tau delta + 2^-18)
     of the exact one, i.e. M is within relative eps.  Top-k compares S
@@ -122,7 +122,7 @@ def tokenmass_rel(w, x, s):
     rel = np.zeros((w.heads, w.n_qb))
     for i in range(w.n_qb):
         lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
-        eps = 2.0 * (tau * 2.0 ** -19 * qn[:, lo:hi].max(axis=1) * kn + 2.0 ** -18)
+        eps = 2.0 * (tau * 2.0 ** -15 * qn[:, lo:hi].max(axis=1) * kn + 2.0 ** -18)
         if w.select_mode == I.SELECT_TOP_K:
             rel[:, i] = eps / np.abs(s[:, i]).max(axis=1)
         else:
