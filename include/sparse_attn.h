@@ -61,9 +61,9 @@ typedef enum sa_score_mode {
   SA_SCORE_POOLED = 0,      /* block means, scaled dot product                    */
   SA_SCORE_LOWRANK = 1,     /* mean over the block pair of rank-r predicted scores */
   SA_SCORE_LOWRANK_MAX = 2, /* max over the block pair of rank-16 predicted token
-                               scores (fp32 token scores; rank must be 16)         */
+                               scores (rank must be 16)                            */
   SA_SCORE_LOWRANK_MASS = 3 /* ln of the block pair's predicted softmax mass from
-                               rank-16 token scores (fp32; rank must be 16)        */
+                               rank-16 token scores (rank must be 16)              */
 } sa_score_mode;
 typedef enum sa_stage {
   SA_STAGE_SELECT = 0,   /* sparse_attn_select         */
@@ -112,15 +112,19 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
  *                     token-pair scores
  *   SA_SCORE_LOWRANK_MAX: S[h,i,j] = max over valid tokens a of block i and b
  *                     of block j of <q_a Wq[h], k_b Wk[h]> (rank 16; the
- *                     projections are fp64 sums stored as fp32, the token-pair
- *                     scores fp32 on the matrix cores, S their fp32 max)
+ *                     projections are fp64 sums rounded to fp32, each split
+ *                     into bf16 hi + lo; a token-pair score is the fp32 sum of
+ *                     the hi.hi, hi.lo and lo.hi products on the matrix cores,
+ *                     within about 2^-16 sum_c |q~_c k~_c| of the exact one;
+ *                     S is their max)
  *   SA_SCORE_LOWRANK_MASS: with the predicted token scores read as logits
  *                     z_ab = tau <q_a Wq[h], k_b Wk[h]> (tau = score_scale,
  *                     0 -> 1/sqrt(d); valid keys only), S[h,i,j] = ln of the
  *                     mean over valid queries a of block i of the softmax
  *                     mass sum_{b in j} exp(z_ab) / sum_b exp(z_ab).  Rows of
  *                     exp(S) sum to one, so SA_TOP_P's softmax gives back the
- *                     masses.  Rank 16; fp32 token scores and exponentials;
+ *                     masses.  Rank 16; token scores as for
+ *                     SA_SCORE_LOWRANK_MAX, fp32 exponentials and sums;
  *                     the workspace holds ln sum_{b in j} exp(z_ab) for every
  *                     query token and key block (4*H*nKB*q_rows bytes).
  *   SA_TOP_P: P = softmax_j S[h,i,:]; blocks ordered by P descending, ties to
