@@ -1,26 +1,27 @@
 // Attention over the selected key blocks only ("Dynamic Sparsity in
 // Large-Scale Video DiT Training", section "The idea": sparse attention
 // kernels that never build the full score matrix; neighbouring queries, one
-// query block, share one selected key/value set) with work items ordered
-// longest-first so uneven per-head sparsity does not leave CUs idle (same
-// page, "Once the work is uneven"; the Top-p sparse-attention abstract, mlsift
+// query block, share one selected key/value set) with the work balanced over
+// the device so uneven per-head sparsity does not leave CUs idle (same page,
+// "Once the work is uneven"; the Top-p sparse-attention abstract, mlsift
 // listing: rank-level stragglers).
 //
-// queue_kernel : one workgroup sorts the (head, query block) items by their
-//                selected-block count, largest first, ties by item id
-//                (bitonic sort of packed 32-bit keys in LDS).  Workgroups of
-//                the attention grid take items in that order, so the hardware
-//                dispatcher hands the longest items out first.
+// queue_kernel : one workgroup orders the work units (items, or halves of
+//                their block lists) into per-XCD ranges by a counting sort on
+//                (range, head, half, count); see "work queue" below.
 // attn_f32     : fp32 path (one thread per query, 32-key LDS sub-tiles,
-//                online softmax in fp32).
-// attn_bf16    : bf16 MFMA path, d = 128, block = 128.  One workgroup of four
-//                waves per item; wave w owns queries 32w..32w+31.  Per key
-//                block: K (row-major) and V (transposed, XOR-swizzled 4-key
-//                groups) are staged in LDS; S^T = K Q^T with
-//                v_mfma_f32_32x32x16_bf16 so that each lane holds one query's
-//                scores (row max = local max + one cross-half exchange);
-//                online softmax in the exp2 domain; P^T goes straight from the
-//                accumulator registers into the B operand of O^T = V^T P^T.
+//                online softmax in fp32), one workgroup per item.
+// attn_bf16    : bf16 MFMA path, d = 128, block = 128, persistent: each
+//                workgroup of four waves takes units from its XCD's queue;
+//                wave w owns queries 32w..32w+31.  Per key block: K and V go
+//                into LDS by direct loads (XOR-swizzled rows); S^T = K Q^T
+//                with v_mfma_f32_32x32x16_bf16 so that each lane holds one
+//                query's scores (row max = local max + one cross-half
+//                exchange); online softmax in the exp2 domain; P^T goes
+//                straight from the accumulator registers into the B operand
+//                of O^T = V^T P^T, with V read through transposing LDS reads.
+//                Halves of an item combine their partial states in a fixed
+//                order (attend_item).
 #include <float.h>
 #include <limits.h>
 #include <math.h>

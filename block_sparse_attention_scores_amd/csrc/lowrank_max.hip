@@ -6,9 +6,10 @@
 //
 //   project_kernel  X~[h, row, :] = X[h, src, :] W[h], fp64 sums (in input
 //                   order) rounded to fp32 and stored split into bf16 hi and
-//                   lo (token_mma.h); one thread per row with W[h] in LDS.  src = row for valid rows, else the first row of
-//                   the row's block: a duplicate token cannot change a max,
-//                   so the block maxima need no masking.
+//                   lo (token_mma.h); one thread per row with W[h] in LDS.
+//                   src = row for valid rows, else the first row of the
+//                   row's block: a duplicate token cannot change a max, so
+//                   the block maxima need no masking.
 //   blockmax_kernel one workgroup per (head, query block, run of key blocks);
 //                   each wave scores its 32 query tokens against the 128 keys
 //                   of a key block (split-bf16 matrix-core products, see
