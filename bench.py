@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the untimed load-balance and dense-context measurements")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--cpu-items", type=int, default=256,
                     help="(head, query block) items in the oracle's timed sample")
     ap.add_argument("--tiles", default=None, metavar="TT,TH,TW",
@@ -289,6 +291,8 @@ def main():
             "tflops": round(bflops / (bms / 1e3) / 1e12, 3),
             "frac_of_peak": round(bflops / (bms / 1e3) / 1e12 / peak, 4),
             "flops_counted": "10*B^2*d per selected pair (five GEMMs; recomputed S and dP not counted)"}
+    if args.graph:
+        rec["graph"] = graph_step(sa, packed, flush, args.steps, ms_step)
     if w.dtype == "bf16" and not args.no_extras:
         rec["load_balance"] = load_balance(sa, packed, flush, fwd_ms)
         rec["dense_context"] = dense_context(w, d, sa, flush, fwd_ms, flops)
@@ -317,6 +321,43 @@ def _timed(fn, flush, reps):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     return float(np.median(ts))
+
+
+def graph_step(sa, packed, flush, steps, eager_ms):
+    """select -> pack -> forward captured once into a HIP graph (the library
+    only enqueues kernels on the caller's stream), replayed `steps` times
+    with the cache flush outside the graph; ms per replay."""
+    import numpy as np
+    import torch
+
+    def run():
+        sa.select()
+        if packed:
+            sa.pack()
+        sa.forward(packed=packed)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    ts = []
+    for k in range(steps):
+        _flush(flush, k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts = np.array(ts)
+    return {"ms_per_step": round(float(ts.mean()), 4),
+            "p10_p90": [round(float(np.percentile(ts, 10)), 4), round(float(np.percentile(ts, 90)), 4)],
+            "eager_ms_per_step": round(eager_ms, 4), "replays": steps}
 
 
 def load_balance(sa, packed, flush, fwd_ms, reps=3):
