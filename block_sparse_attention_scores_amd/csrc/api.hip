@@ -38,6 +38,8 @@ int check_problem(const sa_problem* p, Dims* g) {
   const int64_t nqb = p->q_rows / B, nkb = p->kv_rows / B;
   if (nkb > kMaxKB) return SA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_heads * nqb * nkb >= ((int64_t)1 << 31)) return SA_ERR_UNSUPPORTED;
+  // work units are numbered 2 * item + half in 32 bits
+  if ((int64_t)p->num_heads * nqb >= ((int64_t)1 << 30)) return SA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_heads * p->kv_rows * p->head_dim >= ((int64_t)1 << 40)) return SA_ERR_UNSUPPORTED;
   if (p->select_mode != SA_TOP_P && p->select_mode != SA_TOP_K) return SA_ERR_INVALID_ARG;
   if (p->select_mode == SA_TOP_P && !(p->top_p > 0.f)) return SA_ERR_INVALID_ARG;

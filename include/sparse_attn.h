@@ -75,7 +75,9 @@ typedef enum sa_stage {
 
 /* Problem description (host struct, read during the call only).
  * Notation: H = num_heads (batch folded in), d = head_dim, B = block,
- * nQB = q_rows / B, nKB = kv_rows / B, W = ceil(nKB / 32). */
+ * nQB = q_rows / B, nKB = kv_rows / B, W = ceil(nKB / 32).
+ * Size limits (else SA_ERR_UNSUPPORTED): nKB <= 4096, H*nQB*nKB < 2^31,
+ * H*nQB < 2^30, H*kv_rows*d < 2^40. */
 typedef struct sa_problem {
   int32_t num_heads;    /* H >= 1                                             */
   int32_t head_dim;     /* d: 64 or 128 (bf16 attention: 128)                */
@@ -87,13 +89,15 @@ typedef struct sa_problem {
   int64_t kv_rows;      /* nKB * B, nKB <= 4096                               */
   int64_t kv_valid;     /* kv_rows - B < kv_valid <= kv_rows                  */
   float sm_scale;       /* attention logit scale; <= 0 means 1/sqrt(d)        */
-  float score_scale;    /* pooled block-score scale; <= 0 means 1/sqrt(d)     */
+  float score_scale;    /* pooled block-score scale and the temperature of
+                           SA_SCORE_LOWRANK_MASS; <= 0 means 1/sqrt(d)        */
   int32_t select_mode;  /* sa_select_mode                                     */
   float top_p;          /* SA_TOP_P: mass to reach, > 0; >= 1 keeps all       */
   int32_t top_k;        /* SA_TOP_P: floor (>= 0); SA_TOP_K: k (>= 1); both
                            are clamped to nKB                                 */
   int32_t score_mode;   /* sa_score_mode                                      */
-  int32_t rank;         /* low-rank modes: predictor rank r, 1..64 (16 for MAX) */
+  int32_t rank;         /* low-rank modes: predictor rank r, 1..64 (16 for the
+                           token-level MAX and MASS modes)                    */
 } sa_problem;
 
 /* Workspace bytes needed by one entry point (`stage`) for this problem.

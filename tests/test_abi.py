@@ -93,6 +93,9 @@ def test_workspace_sizes(lib):
     (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=8), B.SA_ERR_UNSUPPORTED),
     (dict(score_mode=B.SA_SCORE_LOWRANK_MAX, rank=0), B.SA_ERR_INVALID_ARG),
     (dict(score_mode=B.SA_SCORE_LOWRANK_MASS, rank=32), B.SA_ERR_UNSUPPORTED),
+    # 2^30 (head, query block) items with a single key block: unit ids would overflow
+    (dict(heads=1 << 14, q_rows=(1 << 16) * 128, q_valid=(1 << 16) * 128, kv_rows=128,
+          kv_valid=128), B.SA_ERR_UNSUPPORTED),
     (dict(score_mode=4), B.SA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), B.SA_ERR_INVALID_ARG),
 ])
