@@ -11,7 +11,9 @@
 // predictor the workgroup also projects its mean through W (fp64).
 //
 // score_kernel: S = scale * X Y^T per head in fp64 (X = pooled or projected
-// query blocks, Y = key blocks) on the fp64 matrix cores.
+// query blocks, Y = key blocks) on the fp64 matrix cores.  score_lds_kernel:
+// the same scores, bit for bit, for inner 64 or 128 with the operand rows of
+// a 64 x 64 block staged in LDS (a quarter of the L2 reads).
 #include "sa_common.h"
 
 namespace sa {
@@ -170,6 +172,75 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ X
   }
 }
 
+// The same scores for inner = 64 or 128, a 64 x 64 block of S per workgroup:
+// the 64 rows of X and of Y pass through LDS in chunks of 32 inner indices,
+// so each is read once per block instead of once per 16 x 16 tile (a quarter
+// of the L2 reads).  Wave w owns row tile w and the four column tiles; each
+// tile takes exactly the MFMA sequence of score_kernel (steps 2s and 2s+1 on
+// inner indices 8s + 2g and 8s + 2g + 1), so the scores are bit-identical.
+constexpr int kScoreChunk = 32;                 // inner indices per LDS chunk
+constexpr int kScoreRow = kScoreChunk + 2;      // padded LDS row (doubles)
+
+template <int NC>  // chunks: inner = 32 NC
+__global__ __launch_bounds__(256) void score_lds_kernel(const double* __restrict__ X,
+                                                        const double* __restrict__ Y, int nx,
+                                                        int ny, double scale,
+                                                        double* __restrict__ S) {
+  constexpr int inner = kScoreChunk * NC;
+  __shared__ __attribute__((aligned(16))) double xs[64 * kScoreRow];
+  __shared__ __attribute__((aligned(16))) double ys[64 * kScoreRow];
+  const int h = blockIdx.z, w = threadIdx.x / kWave, l = lane_id();
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int r = l % 16, g = l / 16;
+  // staging: thread t copies inner indices 8(t%4) .. +8 of every chunk of row
+  // t/4 of X and of Y; all chunks are loaded up front (one load latency)
+  const int sr = threadIdx.x / 4, sc = 8 * (threadIdx.x % 4);
+  const bool xin = i0 + sr < nx, yin = j0 + sr < ny;
+  const double* xp = X + ((int64_t)h * nx + i0 + sr) * inner + sc;
+  const double* yp = Y + ((int64_t)h * ny + j0 + sr) * inner + sc;
+  f64x2 xr[NC][4], yr[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xr[c][e] = xin ? *reinterpret_cast<const f64x2*>(xp + kScoreChunk * c + 2 * e) : f64x2{0.0, 0.0};
+      yr[c][e] = yin ? *reinterpret_cast<const f64x2*>(yp + kScoreChunk * c + 2 * e) : f64x2{0.0, 0.0};
+    }
+  f64x4 acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c > 0) __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<f64x2*>(xs + sr * kScoreRow + sc + 2 * e) = xr[c][e];
+      *reinterpret_cast<f64x2*>(ys + sr * kScoreRow + sc + 2 * e) = yr[c][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kScoreChunk / 8; ++s) {
+      const f64x2 a = *reinterpret_cast<const f64x2*>(xs + (16 * w + r) * kScoreRow + 8 * s + 2 * g);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const f64x2 b = *reinterpret_cast<const f64x2*>(ys + (16 * ct + r) * kScoreRow + 8 * s + 2 * g);
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, b.x, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, b.y, acc[ct], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int j = j0 + 16 * ct + r;
+    if (j >= ny) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + 16 * w + 4 * q + g;
+      if (i < nx) S[((int64_t)h * nx + i) * ny + j] = scale * acc[ct][q];
+    }
+  }
+}
+
 template <typename T, int D, int BLK>
 hipError_t pool_launch(const Dims& g, const void* q, const void* k, const float* wq,
                        const float* wk, double* qbar, double* kbar, double* qt, double* kt,
@@ -203,6 +274,14 @@ hipError_t launch_pool(const Dims& g, const void* q, const void* k, const float*
 
 hipError_t launch_scores(const Dims& g, const double* qx, const double* kx, int inner,
                          double scale, double* scores, hipStream_t s) {
+  if (inner == 64 || inner == 128) {
+    const dim3 grid((g.nkb + 63) / 64, (g.nqb + 63) / 64, g.H);
+    if (inner == 64)
+      hipLaunchKernelGGL(score_lds_kernel<2>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, scale, scores);
+    else
+      hipLaunchKernelGGL(score_lds_kernel<4>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, scale, scores);
+    return hipGetLastError();
+  }
   const dim3 grid((g.nkb + 63) / 64, (g.nqb + 15) / 16, g.H);
   if (inner <= 8) {
     hipLaunchKernelGGL(score_kernel<2>, grid, dim3(256), 0, s, qx, kx, g.nqb, g.nkb, inner, scale, scores);
