@@ -12,7 +12,8 @@
 // Rows of up to 1024 blocks are sorted in registers (select_reg_kernel: lane
 // l holds sorted positions l, l+64, ...; strides under 64 exchange across
 // lanes (DPP moves, or ds_bpermute for 16 and 32), larger ones swap
-// registers).  Longer rows go through LDS
+// registers).  Only the keys are sorted; the kept blocks then follow from
+// each lane's unsorted keys and the cut key.  Longer rows go through LDS
 // (select_kernel).
 #include <float.h>
 
@@ -164,15 +165,12 @@ __device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// a goes before b: larger key first, then lower block id
-__device__ __forceinline__ bool before_k(uint64_t ka, int ia, uint64_t kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
 // One compare-exchange stage of the bitonic network (block size SIZE, partner
-// distance STRIDE) over positions e = l + 64 k.
+// distance STRIDE) over positions e = l + 64 k, into descending key order.
+// Only keys move: equal keys are interchangeable, and block ids are resolved
+// afterwards from each lane's unsorted keys (select_reg_kernel).
 template <int K, int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&key)[K], int (&idx)[K], int l) {
+__device__ __forceinline__ void bitonic_stage(uint64_t (&key)[K], int l) {
   if constexpr (STRIDE >= kWave) {
     constexpr int ks = STRIDE / kWave;
 #pragma unroll
@@ -180,11 +178,9 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&key)[K], int (&idx)[K],
       if (k & ks) continue;
       const int kb = k | ks;
       const bool up = ((kWave * k) & SIZE) == 0;   // SIZE >= 128: lane bits do not matter
-      const bool sw = up ? before_k(key[kb], idx[kb], key[k], idx[k])
-                         : before_k(key[k], idx[k], key[kb], idx[kb]);
+      const bool sw = up ? key[kb] > key[k] : key[k] > key[kb];
       if (sw) {
         const uint64_t tk = key[k]; key[k] = key[kb]; key[kb] = tk;
-        const int ti = idx[k]; idx[k] = idx[kb]; idx[kb] = ti;
       }
     }
   } else {
@@ -192,25 +188,23 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&key)[K], int (&idx)[K],
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint64_t pk = xor_lane<STRIDE>(key[k]);
-      const int pi = xor_lane<STRIDE>(idx[k]);
       const bool up = ((l + kWave * k) & SIZE) == 0;
-      // the lower position of an ascending pair keeps the earlier element
-      const bool self_first = before_k(key[k], idx[k], pk, pi);
-      if (self_first != (lower == up)) { key[k] = pk; idx[k] = pi; }
+      // the lower position of a descending pair keeps the larger key
+      key[k] = (lower == up) ? (key[k] > pk ? key[k] : pk) : (key[k] > pk ? pk : key[k]);
     }
   }
 }
 
-// The whole network for 64 K elements: sizes 2, 4, ..., 64 K, each with
-// strides SIZE/2 down to 1.
+// The whole network for 64 K keys: sizes 2, 4, ..., 64 K, each with strides
+// SIZE/2 down to 1.
 template <int K, int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic(uint64_t (&key)[K], int (&idx)[K], int l) {
+__device__ __forceinline__ void bitonic(uint64_t (&key)[K], int l) {
   if constexpr (SIZE <= kWave * K) {
     if constexpr (STRIDE == 0) {
-      bitonic<K, SIZE * 2, SIZE>(key, idx, l);
+      bitonic<K, SIZE * 2, SIZE>(key, l);
     } else {
-      bitonic_stage<K, SIZE, STRIDE>(key, idx, l);
-      bitonic<K, SIZE, STRIDE / 2>(key, idx, l);
+      bitonic_stage<K, SIZE, STRIDE>(key, l);
+      bitonic<K, SIZE, STRIDE / 2>(key, l);
     }
   }
 }
@@ -219,13 +213,11 @@ template <int K>  // elements per lane; the sort length is 64 * K
 __global__ __launch_bounds__(kWave) void select_reg_kernel(
     const double* __restrict__ S, int nkb, int W, int mode, double top_p, int top_k,
     uint32_t* __restrict__ bits_out, int32_t* __restrict__ counts) {
-  constexpr int N2 = kWave * K;
-  __shared__ uint32_t bits[N2 / 32];
+  __shared__ uint64_t okey[kWave * K];   // unsorted keys, element j at j
   const int row = blockIdx.x, l = threadIdx.x;
   const double* s = S + (int64_t)row * nkb;
 
   uint64_t key[K];
-  int idx[K];
   if (mode == SA_TOP_P) {
     double v[K];
     double mx = -DBL_MAX;
@@ -248,20 +240,19 @@ __global__ __launch_bounds__(kWave) void select_reg_kernel(
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
       key[k] = j < nkb ? order_key(v[k] / tot) : 0ull;   // padding sorts last
-      idx[k] = j < nkb ? j : 0x7fffffff;
     }
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
       key[k] = j < nkb ? order_key(s[j]) : 0ull;
-      idx[k] = j < nkb ? j : 0x7fffffff;
     }
   }
-  for (int w = l; w < N2 / 32; w += kWave) bits[w] = 0u;
+#pragma unroll
+  for (int k = 0; k < K; ++k) okey[l + kWave * k] = key[k];
 
-  // bitonic sort into "before" order over positions e = l + 64 k
-  bitonic<K, 2, 1>(key, idx, l);
+  // bitonic sort of the keys into descending order over positions e = l + 64 k
+  bitonic<K, 2, 1>(key, l);
 
   const int kf = min(top_k, nkb);
   int m;
@@ -286,19 +277,49 @@ __global__ __launch_bounds__(kWave) void select_reg_kernel(
   } else {
     m = kf;
   }
+
+  // The kept set is the first m positions of the (key descending, block id
+  // ascending) order: every block whose key exceeds the cut key kc (position
+  // m - 1), then the r lowest-id blocks whose key equals it.  Each lane tests
+  // its unsorted blocks j = l + 64 k; a ballot over k is mask words 2k, 2k+1.
+  uint64_t kc = 0;
+  {
+    const int sk = (m - 1) / kWave, sl = (m - 1) % kWave;   // m >= 1
+    uint64_t kk = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (k == sk) kk = key[k];
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)kk, sl, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(kk >> 32), sl, kWave);
+    kc = ((uint64_t)hi << 32) | lo;
+  }
   __syncthreads();
+  uint64_t gt[K], eq[K];
+  int above = 0;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int e = l + kWave * k, j = idx[k];
-    if (e < m && (unsigned)j < (unsigned)nkb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    const int j = l + kWave * k;
+    const uint64_t ok = okey[j];
+    gt[k] = __ballot(j < nkb && ok > kc);
+    eq[k] = __ballot(j < nkb && ok == kc);
+    above += __popcll(gt[k]);
   }
-  __syncthreads();
+  int r = m - above;   // ties at the cut to keep, lowest ids first
+  const uint64_t below_me = (l == 0) ? 0ull : (~0ull >> (kWave - l));
   int c = 0;
-  for (int w = l; w < W; w += kWave) {
-    bits_out[(int64_t)row * W + w] = bits[w];
-    c += __popc(bits[w]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool tie_kept = ((eq[k] >> l) & 1ull) && __popcll(eq[k] & below_me) < r;
+    const uint64_t b = gt[k] | __ballot(tie_kept);
+    r -= __popcll(eq[k]);
+    if (l == 0) {
+      if (2 * k < W) bits_out[(int64_t)row * W + 2 * k] = (uint32_t)b;
+      if (2 * k + 1 < W) bits_out[(int64_t)row * W + 2 * k + 1] = (uint32_t)(b >> 32);
+    }
+    c += __popcll(b);
   }
-  c = wave_reduce(c, [](int a, int b) { return a + b; });
+  // the count is the popcount of the written row, so the CSR built from it
+  // always matches the mask
   if (l == 0) counts[row] = c;
 }
 
