@@ -13,8 +13,10 @@
 // l holds sorted positions l, l+64, ...; strides under 64 exchange across
 // lanes (DPP moves, or ds_bpermute for 16 and 32), larger ones swap
 // registers).  Only the keys are sorted; the kept blocks then follow from
-// each lane's unsorted keys and the cut key.  Longer rows go through LDS
-// (select_kernel).
+// each lane's unsorted keys and the cut key.  Rows of 257 to 1024 blocks skip
+// the sort: the cut key is found by a bitwise search over the key space (the
+// top-p cut from mass sums, the top-k cut and the floor from counts).  Longer
+// rows go through LDS (select_kernel).
 #include <float.h>
 
 #include "sa_common.h"
@@ -209,81 +211,139 @@ __device__ __forceinline__ void bitonic(uint64_t (&key)[K], int l) {
   }
 }
 
+// Largest key kc with at least m valid keys >= kc: the key at position m - 1
+// of the descending order, found bit by bit from the top (ballot counts).
+template <int K>
+__device__ __forceinline__ uint64_t key_at_rank(const uint64_t (&key)[K], int m) {
+  uint64_t kq = 0;
+  for (int b = 63; b >= 0; --b) {
+    const uint64_t cand = kq | (1ull << b);
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) cnt += __popcll(__ballot(key[k] >= cand));   // padding key 0 < cand
+    if (cnt >= m) kq = cand;
+  }
+  return kq;
+}
+
 template <int K>  // elements per lane; the sort length is 64 * K
 __global__ __launch_bounds__(kWave) void select_reg_kernel(
     const double* __restrict__ S, int nkb, int W, int mode, double top_p, int top_k,
     uint32_t* __restrict__ bits_out, int32_t* __restrict__ counts) {
-  __shared__ uint64_t okey[kWave * K];   // unsorted keys, element j at j
+  // Rows of up to 256 blocks are sorted; longer rows find the cut key by a
+  // bitwise search instead (no sort: 64 reductions over the unsorted keys).
+  constexpr bool kSearch = K >= 8;
+  __shared__ uint64_t okey[kSearch ? 1 : kWave * K];   // unsorted keys, element j at j
   const int row = blockIdx.x, l = threadIdx.x;
   const double* s = S + (int64_t)row * nkb;
 
   uint64_t key[K];
+  double mass[K];   // softmax mass of block j = l + 64 k (top-p mode)
   if (mode == SA_TOP_P) {
-    double v[K];
     double mx = -DBL_MAX;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
-      v[k] = j < nkb ? s[j] : -DBL_MAX;
-      mx = fmax(mx, v[k]);
+      mass[k] = j < nkb ? s[j] : -DBL_MAX;
+      mx = fmax(mx, mass[k]);
     }
     mx = wave_reduce(mx, [](double a, double b) { return fmax(a, b); });
     double part = 0.0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
-      v[k] = j < nkb ? exp(v[k] - mx) : 0.0;
-      part += v[k];
+      mass[k] = j < nkb ? exp(mass[k] - mx) : 0.0;
+      part += mass[k];
     }
     const double tot = wave_reduce(part, [](double a, double b) { return a + b; });
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
-      key[k] = j < nkb ? order_key(v[k] / tot) : 0ull;   // padding sorts last
+      mass[k] = j < nkb ? mass[k] / tot : 0.0;
+      key[k] = j < nkb ? order_key(mass[k]) : 0ull;   // padding sorts last
     }
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int j = l + kWave * k;
+      mass[k] = 0.0;
       key[k] = j < nkb ? order_key(s[j]) : 0ull;
     }
   }
-#pragma unroll
-  for (int k = 0; k < K; ++k) okey[l + kWave * k] = key[k];
-
-  // bitonic sort of the keys into descending order over positions e = l + 64 k
-  bitonic<K, 2, 1>(key, l);
 
   const int kf = min(top_k, nkb);
   int m;
-  if (mode == SA_TOP_P) {
-    if (top_p >= 1.0) {
-      m = nkb;
-    } else {
-      // cumulative mass in sorted order; count the positions still below p
-      double carry = 0.0;
-      int below = 0;
+  uint64_t kc = 0;   // the cut key: that of position m - 1 in descending order
+  if constexpr (kSearch) {
+    // Top-p: the cut is at the largest key kp whose blocks with keys >= kp
+    // hold mass >= p (the mass of the keys above any larger candidate stays
+    // below p).  Ties at kp are taken in block-id order until the cumulative
+    // mass reaches p.  A total below p through rounding keeps every block.
+    bool at_kp = false;
+    if (mode == SA_TOP_P && top_p < 1.0) {
+      uint64_t kp = 0;
+      for (int b = 63; b >= 0; --b) {
+        const uint64_t cand = kp | (1ull << b);
+        double part = 0.0;
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int e = l + kWave * k;
-        const double mass = e < nkb ? key_value(key[k]) : 0.0;
-        const double cs = carry + wave_inclusive_scan(mass);
-        below += __popcll(__ballot(e < nkb && cs < top_p));
-        carry = __shfl(cs, kWave - 1, kWave);
+        for (int k = 0; k < K; ++k) part += key[k] >= cand ? mass[k] : 0.0;
+        if (wave_reduce(part, [](double a, double b2) { return a + b2; }) >= top_p) kp = cand;
       }
-      m = min(nkb, 1 + below);
+      if (kp == 0) {
+        m = nkb;
+      } else {
+        double part = 0.0;
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          part += key[k] > kp ? mass[k] : 0.0;
+          gt += __popcll(__ballot(key[k] > kp));
+          eq += __popcll(__ballot(key[k] == kp));
+        }
+        double cs = wave_reduce(part, [](double a, double b2) { return a + b2; });
+        const double pk = key_value(kp);
+        int r = 1;
+        for (cs += pk; r < eq && cs < top_p; ++r) cs += pk;
+        m = gt + r;
+        at_kp = true;
+        kc = kp;
+      }
+    } else {
+      m = mode == SA_TOP_P ? nkb : kf;
     }
-    m = max(m, kf);
+    if (mode == SA_TOP_P && m < kf) {
+      m = kf;
+      at_kp = false;
+    }
+    if (!at_kp) kc = key_at_rank<K>(key, m);
   } else {
-    m = kf;
-  }
+#pragma unroll
+    for (int k = 0; k < K; ++k) okey[l + kWave * k] = key[k];
 
-  // The kept set is the first m positions of the (key descending, block id
-  // ascending) order: every block whose key exceeds the cut key kc (position
-  // m - 1), then the r lowest-id blocks whose key equals it.  Each lane tests
-  // its unsorted blocks j = l + 64 k; a ballot over k is mask words 2k, 2k+1.
-  uint64_t kc = 0;
-  {
+    // bitonic sort of the keys into descending order over positions e = l + 64 k
+    bitonic<K, 2, 1>(key, l);
+
+    if (mode == SA_TOP_P) {
+      if (top_p >= 1.0) {
+        m = nkb;
+      } else {
+        // cumulative mass in sorted order; count the positions still below p
+        double carry = 0.0;
+        int below = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int e = l + kWave * k;
+          const double ms = e < nkb ? key_value(key[k]) : 0.0;
+          const double cs = carry + wave_inclusive_scan(ms);
+          below += __popcll(__ballot(e < nkb && cs < top_p));
+          carry = __shfl(cs, kWave - 1, kWave);
+        }
+        m = min(nkb, 1 + below);
+      }
+      m = max(m, kf);
+    } else {
+      m = kf;
+    }
     const int sk = (m - 1) / kWave, sl = (m - 1) % kWave;   // m >= 1
     uint64_t kk = 0;
 #pragma unroll
@@ -292,16 +352,22 @@ __global__ __launch_bounds__(kWave) void select_reg_kernel(
     const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)kk, sl, kWave);
     const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(kk >> 32), sl, kWave);
     kc = ((uint64_t)hi << 32) | lo;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) key[k] = okey[l + kWave * k];   // back to unsorted
   }
-  __syncthreads();
+
+  // The kept set is the first m positions of the (key descending, block id
+  // ascending) order: every block whose key exceeds the cut key kc, then the
+  // r lowest-id blocks whose key equals it.  Each lane tests its unsorted
+  // blocks j = l + 64 k; a ballot over k is mask words 2k, 2k+1.
   uint64_t gt[K], eq[K];
   int above = 0;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int j = l + kWave * k;
-    const uint64_t ok = okey[j];
-    gt[k] = __ballot(j < nkb && ok > kc);
-    eq[k] = __ballot(j < nkb && ok == kc);
+    gt[k] = __ballot(j < nkb && key[k] > kc);
+    eq[k] = __ballot(j < nkb && key[k] == kc);
     above += __popcll(gt[k]);
   }
   int r = m - above;   // ties at the cut to keep, lowest ids first

@@ -313,6 +313,21 @@ def test_row_lengths_across_sort_widths(nkb, mode):
         assert np.all(mask.sum(axis=2) == 37)
 
 
+@pytest.mark.parametrize("nkb,p,k", [(700, 0.1, 50), (300, 1.0, 2), (900, 0.95, 1)])
+def test_cut_search_rows(nkb, p, k):
+    """Rows of 300 to 900 key blocks, whose cut is found by the bitwise key
+    search: a top-k floor above the top-p count, p = 1, and a deep top-p cut."""
+    w = I.Workload(f"cut{nkb}", heads=2, head_dim=64, block=64, dtype="f32",
+                   latent=(nkb // 100, 80, 80), q_start=0, q_valid=300, seed=70 + nkb,
+                   strength=2.0, tile=(1, 8, 8), clusters=16, select_mode=I.SELECT_TOP_P,
+                   top_p=p, top_k=k)
+    assert w.n_kb == nkb
+    sa, _, mask = full_check(w)
+    assert np.all(mask.sum(axis=2) >= min(k, nkb))
+    if p >= 1.0:
+        assert np.all(mask[:, : w.n_qb])
+
+
 def test_csr_from_external_mask_bit_exact():
     w = small_bf16(name="ext_mask", seed=30)
     x = I.generate(w)
