@@ -271,9 +271,6 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
 constexpr int kPartO = 16 * 256 * 4;              // fp32 O of the 256 lanes
 constexpr int kSlotFloats = kPartO + 2 * 256;     // + running max and sum per lane
 
-// read-only int32 data in the constant address space (scalar loads)
-typedef const __attribute__((address_space(4))) int32_t* cidx_t;
-
 __device__ __forceinline__ void attend_item(
     int unit, int split, float* __restrict__ partial, int32_t* __restrict__ done, int* flag,
     uint16_t* kl, uint16_t* vl, const uint16_t* __restrict__ q,
@@ -334,17 +331,11 @@ __device__ __forceinline__ void attend_item(
   const Range range = unit_range(row_ptr, item, part, split);
   const int e0 = __builtin_amdgcn_readfirstlane(range.lo);
   const int e1 = __builtin_amdgcn_readfirstlane(range.hi);
-  // The block lists are read-only for the whole launch: read through the
-  // constant address space they become scalar loads, whose wait (lgkmcnt)
-  // does not also wait for the block loads in flight (vmcnt), as a vector
-  // load of the next entry would at the top of every block.
-  const cidx_t ci = (cidx_t)col_idx;
-  const cidx_t cs = (cidx_t)col_slot;
   // source block of entry e (-1: skip)
   auto block_of = [&](int e) -> int64_t {
-    const int j = __builtin_amdgcn_readfirstlane(ci[e]);
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
     if ((unsigned)j >= (unsigned)nkb) return -1;
-    return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(cs[e]) : (int64_t)h * nkb + j;
+    return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(col_slot[e]) : (int64_t)h * nkb + j;
   };
 
   int e = e0;
@@ -358,7 +349,7 @@ __device__ __forceinline__ void attend_item(
   __syncthreads();
 
   while (e < e1) {
-    const int j = __builtin_amdgcn_readfirstlane(ci[e]);
+    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
     int en = e + 1;
     int64_t bn = -1;
     while (en < e1 && (bn = block_of(en)) < 0) ++en;
