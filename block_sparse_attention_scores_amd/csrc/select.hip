@@ -5,18 +5,20 @@
 //
 // One single-wave workgroup per (head, query block) row.  Top-p mode turns
 // the row's scores into softmax masses (fp64, max-subtracted, sum in a fixed
-// order).  A bitonic sort orders (value descending, block id ascending); the
-// cumulative mass in that order comes from a wave scan in fp64.  The kept set
-// is written as a bitmask row plus its count.
+// order).  The kept set is the first m blocks in the order (value
+// descending, block id ascending); for top-p, m is the shortest prefix whose
+// cumulative mass (fp64) reaches p, raised to the floor.  It is written as a
+// bitmask row plus its count.
 //
-// Rows of up to 1024 blocks are sorted in registers (select_reg_kernel: lane
-// l holds sorted positions l, l+64, ...; strides under 64 exchange across
-// lanes (DPP moves, or ds_bpermute for 16 and 32), larger ones swap
-// registers).  Only the keys are sorted; the kept blocks then follow from
-// each lane's unsorted keys and the cut key.  Rows of 257 to 1024 blocks skip
-// the sort: the cut key is found by a bitwise search over the key space (the
-// top-p cut from mass sums, the top-k cut and the floor from counts).  Longer
-// rows go through LDS (select_kernel).
+// Rows of up to 1024 blocks stay in registers (select_reg_kernel).  Rows of
+// up to 256 blocks are sorted there (lane l holds sorted positions l, l+64,
+// ...; strides under 64 exchange across lanes by DPP moves, or ds_bpermute
+// for 16 and 32, larger ones swap registers).  Only the keys are sorted; the
+// kept blocks then follow from each lane's unsorted keys and the cut key.
+// Rows of 257 to 1024 blocks skip the sort: the cut key is found by a bitwise
+// search over the key space (the top-p cut from mass sums, the top-k cut and
+// the floor from counts).  Longer rows go through an LDS sort of (value, id)
+// pairs (select_kernel).
 #include <float.h>
 
 #include "sa_common.h"
