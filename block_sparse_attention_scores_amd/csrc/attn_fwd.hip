@@ -360,9 +360,6 @@ __device__ __forceinline__ void attend_item(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-    // Raised wave priority for the score MFMAs: the other workgroup's wave on
-    // this SIMD, usually in its softmax, fills the issue slots these leave.
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
 #pragma unroll
@@ -372,7 +369,6 @@ __device__ __forceinline__ void attend_item(
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
       }
 
-    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
     __syncthreads();
     if (en < e1) dma_block(k + bn * (kB * kD), kl, wave, kvo);
@@ -409,6 +405,11 @@ __device__ __forceinline__ void attend_item(
       m_run = mn;
     }
     const float mn = m_run;
+    // Raised wave priority for the softmax and P V phase, where exponentials
+    // and MFMAs alternate: the other workgroup's wave on this SIMD, when it is
+    // in its score MFMAs, fills the slots this one leaves (measured 0.5-1%
+    // faster than raising the score phase instead).
+    __builtin_amdgcn_s_setprio(1);
 
     // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
     // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
@@ -439,6 +440,7 @@ __device__ __forceinline__ void attend_item(
       }
     }
     l_run += ps;
+    __builtin_amdgcn_s_setprio(0);
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's K loads of the next block
     __syncthreads();
