@@ -236,6 +236,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __syncthreads();
     if (en < e1) dma_block(v + sn, vl, wave, off.dma);
     const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
+    // raised wave priority over the phase that mixes exponentials and MFMAs
+    // (the other workgroup's wave on the SIMD fills in from its dP MFMAs)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x16 sacc;
@@ -261,6 +264,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                                                            0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's V_{j+1} loads
     __syncthreads();
     if (en < e1) dma_block(k + sn, kl, wave, off.dma);
