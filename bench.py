@@ -49,7 +49,7 @@ def parse():
                     help="skip the untimed load-balance and dense-context measurements")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
-    ap.add_argument("--cpu-items", type=int, default=256,
+    ap.add_argument("--cpu-items", type=int, default=768,
                     help="(head, query block) items in the oracle's timed sample")
     ap.add_argument("--tiles", default=None, metavar="TT,TH,TW",
                     help="video-aware block organisation: Q, K, V are gathered into 3-D tile "
