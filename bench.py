@@ -294,7 +294,7 @@ def main():
     if args.graph:
         rec["graph"] = graph_step(sa, packed, flush, args.steps, ms_step)
     if w.dtype == "bf16" and not args.no_extras:
-        rec["load_balance"] = load_balance(sa, packed, flush, fwd_ms)
+        rec["load_balance"] = load_balance(sa, packed, flush)
         rec["dense_context"] = dense_context(w, d, sa, flush, fwd_ms, flops)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items)
@@ -360,7 +360,7 @@ def graph_step(sa, packed, flush, steps, eager_ms):
             "eager_ms_per_step": round(eager_ms, 4), "replays": steps}
 
 
-def load_balance(sa, packed, flush, fwd_ms, reps=3):
+def load_balance(sa, packed, flush, reps=5):
     """Busy time of each persistent workgroup (device clock stamps at its
     start and when it finds no more work): max / mean over workgroups, the
     single-GPU reading of the load imbalance the Top-p abstract reports
@@ -380,13 +380,18 @@ def load_balance(sa, packed, flush, fwd_ms, reps=3):
         busy = c[:, 1] - c[:, 0]
         imb.append(busy.max() / busy.mean())
         span.append((c[:, 1].max() - c[:, 0].min()) / busy.mean())
-    per_unit = _timed(lambda: sa.forward(packed=packed, schedule=binding.SA_SCHEDULE_PER_UNIT),
-                      flush, reps)
+    # the two schedules timed the same way (flush, then the forward alone),
+    # alternating so that neither gains from running second
+    pers, unit = [], []
+    for r in range(reps):
+        pers.append(_timed(lambda: sa.forward(packed=packed), flush, 1))
+        unit.append(_timed(lambda: sa.forward(packed=packed,
+                                              schedule=binding.SA_SCHEDULE_PER_UNIT), flush, 1))
     return {"workgroups": n, "busy_max_over_mean": round(float(np.median(imb)), 4),
             "span_over_mean_busy": round(float(np.median(span)), 4),
-            "persistent_forward_ms": round(fwd_ms, 4),
+            "persistent_forward_ms": round(float(np.median(pers)), 4),
             "per_unit_workgroups": sa.workgroups(binding.SA_SCHEDULE_PER_UNIT),
-            "per_unit_forward_ms": round(per_unit, 4), "reps": reps}
+            "per_unit_forward_ms": round(float(np.median(unit)), 4), "reps": reps}
 
 
 def dense_context(w, d, sa, flush, fwd_ms, flops, reps=3):
