@@ -40,28 +40,30 @@ using namespace bf16mma;
 // ---------------------------------------------------------------------------
 // A work unit is a (head, query block) item, or one half of its selected-block
 // list when items are split (see split_items below); unit id = 2*item + half.
-// Units are split into kXcd contiguous ranges of the head-major item order,
-// balanced by selected-block count (the work), one range per XCD: concurrent
-// workgroups of an XCD then attend to the same head's key/value blocks, which
-// stay resident in that XCD's L2.  Inside a range, units go head by head,
-// first halves before second halves, and longest first within those: the
-// workgroups of an XCD then stream one range of one head's blocks at a time
-// (mixing heads by length, or the two halves of a head, would multiply the
-// blocks in flight per L2).  A counting sort on (range, head group, half,
-// count) writes the order; xq[x] .. xq[x+1] is range x; ctr[x] (zeroed here)
-// is its cursor; done[item] (zeroed here when split) counts the published
-// halves of an item.
+// The selected entries of all items, in item order, are cut into kXcd equal
+// shares of work, one range per XCD: a unit belongs to the range of the middle
+// of its entries.  Concurrent workgroups of an XCD then attend to the same
+// head's key/value blocks, which stay resident in that XCD's L2.  Inside a
+// range, units go head by head, first halves before second halves, and in
+// query-block order within those: neighbouring query blocks select similar
+// key blocks, so the workgroups of an XCD share more of them in L2 (heads are
+// grouped by 2^hshift when there are thousands of them).  xq[x] .. xq[x+1] is
+// range x; ctr[x] (zeroed here) is its cursor; done[item] (zeroed here when
+// split) counts the published halves of an item.
 //
-// Sort bins: along the item order both the range x and the head h are
-// non-decreasing, so x + h numbers the (range, head) pairs in order.  Heads
-// are grouped by 2^hshift and counts by 2^cshift when the bins would not fit
-// in LDS otherwise.
+// The order is a sort on (group, item) with group = 2 (range + head group) +
+// half.  Along the item order both the range and the head are non-decreasing
+// (for either half), so every group is a contiguous run of items: a unit's
+// position is its group's start plus the number of the group's units before
+// it, which for first halves is its item offset from the group's first item
+// and for second halves the number of split items in between.  No atomic
+// decides any position, so the order is deterministic.
 constexpr int kXcd = 8;
 constexpr int kQueueThreads = 1024;
-constexpr int kQueueMaxBins = kXcd * (4096 + 1);
+constexpr int kQueueMaxGroups = 4096;
 
 struct QueueShape {
-  int nqb, nkb, hshift, cshift, nc;   // nc = count bins per head group
+  int nqb, hshift;
 };
 
 // Selected-block range [lo, hi) of half `part` of item r (the whole list when
@@ -82,11 +84,9 @@ __device__ __forceinline__ int unit_xcd(Range u, int64_t total) {
   return total > 0 ? (int)min<int64_t>(kXcd - 1, mid * kXcd / total) : 0;
 }
 
-__device__ __forceinline__ int queue_key(Range u, int r, int part, const QueueShape& qs,
-                                         int64_t total) {
-  const int c = min(u.hi - u.lo, qs.nkb);
-  const int pair = unit_xcd(u, total) + ((r / qs.nqb) >> qs.hshift);
-  return (2 * pair + part) * qs.nc + ((qs.nkb - c) >> qs.cshift);
+__device__ __forceinline__ int unit_group(Range u, int r, int part, const QueueShape& qs,
+                                          int64_t total) {
+  return 2 * (unit_xcd(u, total) + ((r / qs.nqb) >> qs.hshift)) + part;
 }
 
 __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __restrict__ row_ptr,
@@ -95,40 +95,50 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
                                                               int32_t* __restrict__ xq,
                                                               int32_t* __restrict__ ctr,
                                                               int32_t* __restrict__ done) {
-  __shared__ int hist[kQueueMaxBins];
+  __shared__ int gstart[kQueueMaxGroups];   // group sizes, then their starts
+  __shared__ int gfirst[kQueueMaxGroups];   // first item of each group
+  __shared__ int gsplit[kQueueMaxGroups];   // split items before a second-half group's first
   __shared__ int xcnt[kXcd];
   __shared__ int red[kQueueThreads / kWave + 1];
   const int t = threadIdx.x;
   const int heads = rows / qs.nqb;
-  const int nb = 2 * (kXcd + ((heads - 1) >> qs.hshift) + 1) * qs.nc;
+  const int ng = 2 * (kXcd + ((heads - 1) >> qs.hshift) + 1);
   const int64_t total = row_ptr[rows];
-  for (int b = t; b < nb; b += kQueueThreads) hist[b] = 0;
+  for (int b = t; b < ng; b += kQueueThreads) {
+    gstart[b] = 0;
+    gfirst[b] = INT_MAX;
+  }
   if (t < kXcd) xcnt[t] = 0;
   if (split)
     for (int r = t; r < rows; r += kQueueThreads) done[r] = 0;
   __syncthreads();
+  // group sizes and first items (order-independent, so deterministic)
   for (int r = t; r < rows; r += kQueueThreads) {
     const Range u0 = unit_range(row_ptr, r, 0, split);
-    atomicAdd(&hist[queue_key(u0, r, 0, qs, total)], 1);
+    const int g0 = unit_group(u0, r, 0, qs, total);
+    atomicAdd(&gstart[g0], 1);
+    atomicMin(&gfirst[g0], r);
     atomicAdd(&xcnt[unit_xcd(u0, total)], 1);
     if (u0.halved) {
       const Range u1 = unit_range(row_ptr, r, 1, split);
-      atomicAdd(&hist[queue_key(u1, r, 1, qs, total)], 1);
+      const int g1 = unit_group(u1, r, 1, qs, total);
+      atomicAdd(&gstart[g1], 1);
+      atomicMin(&gfirst[g1], r);
       atomicAdd(&xcnt[unit_xcd(u1, total)], 1);
     }
   }
   __syncthreads();
-  // exclusive scan of the histogram, contiguous chunk per thread
-  const int per = (nb + kQueueThreads - 1) / kQueueThreads;
-  const int lo = min(nb, t * per), hi = min(nb, lo + per);
+  // exclusive scan of the group sizes, contiguous chunk per thread
+  const int per = (ng + kQueueThreads - 1) / kQueueThreads;
+  const int lo = min(ng, t * per), hi = min(ng, lo + per);
   int local = 0;
-  for (int b = lo; b < hi; ++b) local += hist[b];
+  for (int b = lo; b < hi; ++b) local += gstart[b];
   int all;
   int run = block_inclusive_scan(local, red, &all) - local;
   __syncthreads();
   for (int b = lo; b < hi; ++b) {
-    const int c = hist[b];
-    hist[b] = run;
+    const int c = gstart[b];
+    gstart[b] = run;
     run += c;
   }
   if (t == 0) {
@@ -141,13 +151,31 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
     xq[kXcd] = acc;
   }
   __syncthreads();
-  // scatter; the order among units with equal keys is immaterial
-  for (int r = t; r < rows; r += kQueueThreads) {
-    const Range u0 = unit_range(row_ptr, r, 0, split);
-    units[atomicAdd(&hist[queue_key(u0, r, 0, qs, total)], 1)] = 2 * r;
-    if (u0.halved)
-      units[atomicAdd(&hist[queue_key(unit_range(row_ptr, r, 1, split), r, 1, qs, total)], 1)] =
-          2 * r + 1;
+  // positions, chunk by chunk in item order with a running count of split items
+  int carry = 0;
+  for (int base = 0; base < rows; base += kQueueThreads) {
+    const int r = base + t;
+    Range u0{0, 0, false}, u1{0, 0, false};
+    int g0 = 0, g1 = 0;
+    if (r < rows) {
+      u0 = unit_range(row_ptr, r, 0, split);
+      g0 = unit_group(u0, r, 0, qs, total);
+      if (u0.halved) {
+        u1 = unit_range(row_ptr, r, 1, split);
+        g1 = unit_group(u1, r, 1, qs, total);
+      }
+    }
+    const int flag = u0.halved ? 1 : 0;
+    int chunk;
+    const int before = carry + block_inclusive_scan(flag, red, &chunk) - flag;
+    if (flag && gfirst[g1] == r) gsplit[g1] = before;
+    __syncthreads();
+    if (r < rows) {
+      units[gstart[g0] + (r - gfirst[g0])] = 2 * r;
+      if (flag) units[gstart[g1] + (before - gsplit[g1])] = 2 * r + 1;
+    }
+    carry += chunk;
+    __syncthreads();
   }
 }
 
@@ -601,14 +629,11 @@ bool split_items(const Dims& g) {
 }
 
 
-// Finest head grouping, then count resolution, whose sort bins fit in LDS.
+// Finest head grouping whose (range, head group, half) groups fit in LDS.
 QueueShape queue_shape(const Dims& g) {
-  for (int hs = 0; hs < 31; ++hs)
-    for (int cs = 0; cs <= 13; ++cs) {
-      const int64_t nc = (g.nkb >> cs) + 1, groups = ((int64_t)(g.H - 1) >> hs) + 1;
-      if (2 * (kXcd + groups) * nc <= kQueueMaxBins) return {g.nqb, g.nkb, hs, cs, (int)nc};
-    }
-  return {g.nqb, g.nkb, 31, 13, 1};
+  int hs = 0;
+  while (2 * (kXcd + ((g.H - 1) >> hs) + 1) > kQueueMaxGroups) ++hs;
+  return {g.nqb, hs};
 }
 }  // namespace
 

@@ -365,12 +365,55 @@ def pack(x: np.ndarray, demand_ptr: np.ndarray, demand_idx: np.ndarray, block: i
 # ---------------------------------------------------------------------------
 # A10: work order (the order does not change any result)
 # ---------------------------------------------------------------------------
-def work_order(row_ptr: np.ndarray) -> np.ndarray:
-    """(head, query block) items by selected-block count, largest first, ties
-    by item id: the longest-first order that evens per-head work (DSV
-    explainer, "Once the work is uneven"; Top-p abstract, stragglers)."""
-    counts = np.diff(row_ptr)
-    return np.lexsort((np.arange(counts.shape[0]), -counts)).astype(np.int32)
+QUEUE_RANGES = 8          # one contiguous range of work per XCD (chiplet) of the device
+QUEUE_MAX_GROUPS = 4096   # (range, head group, half) groups the device's sort can hold
+
+
+def work_order(row_ptr: np.ndarray, n_qb: int, split: bool, ranges: int = QUEUE_RANGES,
+               max_groups: int = QUEUE_MAX_GROUPS):
+    """Order of the attention's work units.  The pages ask only that uneven
+    per-head work be spread so that no worker straggles (DSV explainer, "Once
+    the work is uneven": reallocate heads by their sparse workload; Top-p
+    abstract: sparse attention becomes a rank-level straggler problem); the
+    order itself is this reading:
+
+    * An item is one (head, query block) row r (rows head-major).  With
+      ``split`` every row of c >= 2 selected blocks is two units, its first
+      ceil(c/2) entries (half 0) and the rest (half 1); otherwise a row is one
+      unit.  Unit id = 2 r + half.
+    * The selected entries of all rows, in row order, are cut into ``ranges``
+      equal shares of work: a unit whose entries span [lo, hi) belongs to range
+      min(ranges-1, floor(mid * ranges / total)), mid = lo + (hi - lo) // 2.
+    * Units are sorted by (range, head group, half, row): head by head inside a
+      range, first halves before second halves, neighbouring query blocks
+      together.  Head group = head >> s, with s the smallest shift for which
+      2 * (ranges + ((H-1) >> s) + 1) <= max_groups (s = 0 unless there are
+      thousands of heads).
+
+    Returns (units int32 [n_units], range_start int32 [ranges + 1])."""
+    row_ptr = np.asarray(row_ptr, np.int64)
+    rows = row_ptr.shape[0] - 1
+    total = int(row_ptr[-1])
+    heads = rows // n_qb
+    shift = 0
+    while 2 * (ranges + ((heads - 1) >> shift) + 1) > max_groups:
+        shift += 1
+    recs = []   # (range, head group, half, row)
+    for r in range(rows):
+        e0, e1 = int(row_ptr[r]), int(row_ptr[r + 1])
+        c = e1 - e0
+        halved = split and c >= 2
+        parts = [(e0, e0 + (c + 1) // 2), (e0 + (c + 1) // 2, e1)] if halved else [(e0, e1)]
+        for half, (lo, hi) in enumerate(parts):
+            mid = lo + (hi - lo) // 2
+            x = min(ranges - 1, mid * ranges // total) if total > 0 else 0
+            recs.append((x, (r // n_qb) >> shift, half, r))
+    recs.sort()
+    units = np.array([2 * r + half for _, _, half, r in recs], np.int32)
+    start = np.zeros(ranges + 1, np.int32)
+    for x, _, _, _ in recs:
+        start[x + 1] += 1
+    return units, np.cumsum(start).astype(np.int32)
 
 
 # ---------------------------------------------------------------------------

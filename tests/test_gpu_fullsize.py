@@ -14,7 +14,7 @@ from oracle import oracle as O
 from block_sparse_attention_scores_amd import inputs as I
 from block_sparse_attention_scores_amd.path import SparseAttention, to_device
 
-from test_gpu_parity import TOL_LSE, TOL_OUT, check_selection, say
+from test_gpu_parity import TOL_LSE, TOL_OUT, check_queue, check_selection, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,7 @@ def test_full_size_workload(name):
         ref = O.pack(src.cpu().view(torch.int16).numpy(), dp, di, w.block)
         assert ref.tobytes() == packed[:total].cpu().view(torch.int16).numpy().tobytes()
     del ref
+    check_queue(w, sa)
 
     items = sampled_items(w, orp)
     o, lse = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,

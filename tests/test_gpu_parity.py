@@ -174,12 +174,35 @@ def check_attention(w, sa, mask, x, items=None):
     return worst
 
 
+def items_split(w) -> bool:
+    """The forward's documented rule: bf16 items are halved when whole items
+    would leave the last round of the persistent grid (two workgroups per
+    CU) more than 5% idle."""
+    if w.dtype != "bf16":
+        return False
+    rows = w.heads * w.n_qb
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    rounds = -(-rows // slots)
+    return rounds * slots > 1.05 * rows
+
+
+def check_queue(w, sa):
+    """The forward's work-unit order (the start of its workspace: units,
+    then the 9 range starts) equals the oracle's work_order, bit for bit."""
+    rows = w.heads * w.n_qb
+    units, start = O.work_order(sa.row_ptr.cpu().numpy(), w.n_qb, items_split(w))
+    ws = sa.ws[B.SA_STAGE_FORWARD].view(torch.int32).cpu().numpy()
+    np.testing.assert_array_equal(ws[2 * rows:2 * rows + 9], start)
+    np.testing.assert_array_equal(ws[:units.size], units)
+
+
 def full_check(w, packed=True):
     say("case", w.name, "packed" if packed else "unpacked")
     sa, x = run_path(w, packed=packed)
     mask, exc = check_selection(w, sa, x)
     if packed:
         check_csr_demand_pack(w, sa, mask, x)
+    check_queue(w, sa)
     err = check_attention(w, sa, mask, x)
     say(f"  nnz={sa.nnz()} of {w.heads * w.n_qb * w.n_kb}, excused={exc}, max_abs_err={err:.3g}")
     return sa, x, mask

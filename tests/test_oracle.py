@@ -378,9 +378,63 @@ def test_demand_and_pack_by_loops():
             assert p[s].tobytes() == x[h, j * B:(j + 1) * B].tobytes()
 
 
-def test_work_order_is_count_descending_stable():
-    row_ptr = np.array([0, 3, 3, 8, 11, 16, 17], np.int32)   # counts 3,0,5,3,5,1
-    assert O.work_order(row_ptr).tolist() == [2, 4, 0, 3, 5, 1]
+def test_work_order_hand_example():
+    # 2 heads x 3 query blocks, counts 4,0,2 | 6,1,3 (16 entries, 8 ranges of 2).
+    # Whole rows: mids 2,4,5,9,12,14 -> ranges 1,2,2,4,6,7.
+    row_ptr = np.array([0, 4, 4, 6, 12, 13, 16])
+    units, start = O.work_order(row_ptr, 3, split=False)
+    assert units.tolist() == [0, 2, 4, 6, 8, 10]
+    assert start.tolist() == [0, 0, 1, 3, 3, 4, 4, 5, 6]
+    # Halves: row 0 -> [0,2) [2,4) (mids 1, 3: ranges 0, 1); row 1 empty, one unit
+    # (mid 4: range 2); row 2 -> [4,5) [5,6) (range 2 twice); row 3 -> [6,9) [9,12)
+    # (mids 7, 10: ranges 3, 5); row 4 has one entry, one unit (range 6); row 5 ->
+    # [13,15) [15,16) (mids 14, 15: range 7 twice, first half first).
+    units, start = O.work_order(row_ptr, 3, split=True)
+    assert units.tolist() == [0, 1, 2, 4, 5, 6, 7, 8, 10, 11]
+    assert start.tolist() == [0, 1, 2, 5, 6, 6, 7, 8, 10]
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_work_order_invariants(split):
+    r = rng(41)
+    for trial in range(20):
+        H, nqb = int(r.integers(1, 6)), int(r.integers(1, 40))
+        counts = r.integers(0, 60, H * nqb)
+        counts[r.random(H * nqb) < 0.1] = 0
+        row_ptr = np.concatenate([[0], np.cumsum(counts)])
+        total = int(row_ptr[-1])
+        units, start = O.work_order(row_ptr, nqb, split=split)
+        rows = units >> 1
+        halves = units & 1
+        # every row once as half 0; half 1 exactly for the split rows of >= 2 entries
+        assert sorted(rows[halves == 0].tolist()) == list(range(H * nqb))
+        want1 = [i for i in range(H * nqb) if split and counts[i] >= 2]
+        assert sorted(rows[halves == 1].tolist()) == want1
+        assert start[0] == 0 and start[-1] == units.size and np.all(np.diff(start) >= 0)
+        for x in range(8):
+            seg = slice(start[x], start[x + 1])
+            hs, hv, rw = rows[seg] // nqb, halves[seg], rows[seg]
+            key = list(zip(hs.tolist(), hv.tolist(), rw.tolist()))
+            assert key == sorted(key)                      # head, half, row ascending
+            # a range's units cover entries near its share [x, x+1) * total / 8
+            for u, h in zip(rw.tolist(), hv.tolist()):
+                e0, e1 = row_ptr[u], row_ptr[u + 1]
+                c = e1 - e0
+                lo, hi = ((e0, e1) if not (split and c >= 2) else
+                          ((e0, e0 + (c + 1) // 2) if h == 0 else (e0 + (c + 1) // 2, e1)))
+                mid = lo + (hi - lo) // 2
+                if total:
+                    assert x * total <= mid * 8 < (x + 1) * total or (x == 7 and mid * 8 >= total * 7)
+
+
+def test_work_order_groups_heads_when_there_are_thousands():
+    # 3000 heads of one query block: head groups of two keep the groups at
+    # 2 * (8 + 1500) <= 4096, so halves of two heads interleave as (h, h+1) half 0,
+    # then (h, h+1) half 1 within a range
+    row_ptr = np.concatenate([[0], np.cumsum(np.full(3000, 4))])
+    units, start = O.work_order(row_ptr, 1, split=True)
+    assert units[:4].tolist() == [0, 2, 1, 3]
+    assert sorted(units.tolist()) == list(range(6000))
 
 
 # ---------------------------------------------------------------------------
@@ -813,3 +867,30 @@ def test_lowrank_mass_identity_predictor_is_exact_block_mass():
         for i in range(4):
             m = O.exact_block_mass(q, k, 29, 45, B, sc, h, i)
             np.testing.assert_allclose(np.exp(s[h, i]), m, rtol=1e-12, atol=1e-15)
+
+
+def test_exact_block_mass_equals_sdpa_with_block_indicator_values():
+    # An independent pin of exact_block_mass: attention with V[b] = one-hot of
+    # b's key block returns, for each query, the softmax mass of every key
+    # block (torch's SDPA in fp64, padded keys masked out); the block masses
+    # are its mean over the valid queries of the query block.
+    g = np.random.default_rng(64)
+    H, B, d, qv, kv = 2, 8, 5, 27, 37
+    q = np.zeros((H, 32, d), np.float32)
+    k = np.zeros((H, 40, d), np.float32)
+    q[:, :qv] = g.standard_normal((H, qv, d)) * 2
+    k[:, :kv] = g.standard_normal((H, kv, d)) * 2
+    nkb = 40 // B
+    onehot = np.zeros((40, nkb))
+    onehot[np.arange(40), np.arange(40) // B] = 1.0
+    allowed = np.zeros((32, 40), bool)
+    allowed[:, :kv] = True
+    sc = 0.7
+    for h in range(H):
+        per_query = _sdpa64(q[h], k[h], onehot, allowed, sc)        # [32, nkb]
+        for i in range(32 // B):
+            lo, hi = i * B, min((i + 1) * B, qv)
+            want = per_query[lo:hi].mean(axis=0)
+            got = O.exact_block_mass(q, k, qv, kv, B, sc, h, i)
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+            assert abs(got.sum() - 1.0) < 1e-12
