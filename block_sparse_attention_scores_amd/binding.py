@@ -22,6 +22,8 @@ SA_ERR_UNSUPPORTED = -2
 SA_ERR_WORKSPACE = -3
 SA_ERR_HIP = -4
 SA_ERR_CAPACITY = -5
+SA_ERR_SCRATCH = -6
+SA_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 SA_F32, SA_BF16 = 0, 1
 SA_TOP_P, SA_TOP_K = 0, 1
@@ -31,8 +33,8 @@ SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT = 0, 1
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
            "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
-           "sparse_attn_forward_ex", "sparse_attn_backward", "sa_video_block_order",
-           "sa_permute_rows", "sa_status_string", "sa_abi_version")
+           "sparse_attn_forward_ex", "sparse_attn_forward_noalloc", "sparse_attn_backward",
+           "sa_video_block_order", "sa_permute_rows", "sa_status_string", "sa_abi_version")
 
 
 class SaProblem(ctypes.Structure):
@@ -96,6 +98,7 @@ def load(path: str = None):
     lib.sa_forward_workgroups.argtypes = [prob, i32, ctypes.POINTER(i32)]
     lib.sparse_attn_forward_ex.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz,
                                            ctypes.POINTER(SaForwardOpts), P]
+    lib.sparse_attn_forward_noalloc.argtypes = [prob, P, P, P, P, P, P, P, P, P]
     lib.sparse_attn_backward.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.sa_video_block_order.argtypes = [ctypes.POINTER(SaVideoTiling), i64, i64, P, P, P, P, P]
     lib.sa_permute_rows.argtypes = [i32, i64, i32, P, P, i64, P, i64, P]
@@ -104,8 +107,8 @@ def load(path: str = None):
     lib.sa_abi_version.argtypes = []
     for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
                  "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
-                 "sparse_attn_forward_ex", "sparse_attn_backward", "sa_video_block_order",
-                 "sa_permute_rows", "sa_abi_version"):
+                 "sparse_attn_forward_ex", "sparse_attn_forward_noalloc", "sparse_attn_backward",
+                 "sa_video_block_order", "sa_permute_rows", "sa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -196,6 +199,13 @@ def sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, ou
         ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
         _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, ctypes.byref(opts),
         _stream(stream)))
+
+
+def sparse_attn_forward_noalloc(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt,
+                                stream=None):
+    _check("sparse_attn_forward_noalloc", load().sparse_attn_forward_noalloc(
+        ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
+        _ptr(v_src), _ptr(out), _ptr(lse_opt), _stream(stream)))
 
 
 def sparse_attn_backward(prob, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv, ws,

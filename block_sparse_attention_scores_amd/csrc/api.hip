@@ -5,8 +5,15 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sa_common.h"
+
+// Work queue of sparse_attn_forward_noalloc, for callers that cannot
+// allocate: one copy per device, held until the process ends.  Host code
+// never uses this name as an address (on the host it is only a stand-in);
+// it uses the device address looked up per device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace sa {
 bool attn_supported(int dtype, int d, int B);
@@ -149,11 +156,41 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept; NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+void* g_scratch_address[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_address[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_address[dev] = p;
+  }
+  return g_scratch_address[dev];
+}
+
+// Pointer and size checks shared by the forward entry points.
+int check_forward_args(const Dims& g, const void* q, const int32_t* row_ptr,
+                       const int32_t* col_idx, const void* k_src, const void* v_src,
+                       const void* out, const float* lse_opt) {
+  if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
+  if (!q || !row_ptr || !col_idx || !k_src || !v_src || !out) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(out))
+    return SA_ERR_INVALID_ARG;
+  if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int sa_abi_version(void) { return 4; }
+int sa_abi_version(void) { return 5; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -163,6 +200,9 @@ const char* sa_status_string(int status) {
     case SA_ERR_WORKSPACE: return "workspace smaller than sa_workspace_size";
     case SA_ERR_HIP: return "HIP launch failed";
     case SA_ERR_CAPACITY: return "demand union exceeds the packed-buffer capacity";
+    case SA_ERR_SCRATCH:
+      return "problem needs more work-queue memory than the static scratch array of "
+             "sparse_attn_forward_noalloc (SA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -278,11 +318,8 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q, const int32_t*
   Dims g;
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
-  if (!q || !row_ptr || !col_idx || !k_src || !v_src || !out) return SA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(out))
-    return SA_ERR_INVALID_ARG;
-  if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  st = check_forward_args(g, q, row_ptr, col_idx, k_src, v_src, out, lse_opt);
+  if (st != SA_OK) return st;
   int schedule = SA_SCHEDULE_PERSISTENT;
   uint64_t* wg_clock = nullptr;
   if (opts) {
@@ -310,6 +347,27 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
                         void* stream) {
   return sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt,
                                 ws, ws_bytes, nullptr, stream);
+}
+
+int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int32_t* row_ptr,
+                                const int32_t* col_idx, const int32_t* col_slot,
+                                const void* k_src, const void* v_src, void* out, float* lse_opt,
+                                void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  st = check_forward_args(g, q, row_ptr, col_idx, k_src, v_src, out, lse_opt);
+  if (st != SA_OK) return st;
+  // whole items only: the queue is all the workspace the launch gets
+  const size_t need = sa::attn_queue_ws_bytes(g);
+  if (need > SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return SA_ERR_HIP;
+  const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
+  SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
+                             need, sm, SA_SCHEDULE_PERSISTENT, nullptr,
+                             static_cast<hipStream_t>(stream)));
+  return SA_OK;
 }
 
 int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, const void* v,

@@ -642,6 +642,8 @@ bool attn_supported(int dtype, int d, int B) {
   return (d == 64 || d == 128) && (B == 64 || B == 128);
 }
 
+size_t attn_queue_ws_bytes(const Dims& g) { return queue_bytes(g.H * g.nqb); }
+
 size_t attn_ws_bytes(const Dims& g) {
   const int rows = g.H * g.nqb;
   return queue_bytes(rows) + (split_items(g) ? partial_bytes(rows) : 0);

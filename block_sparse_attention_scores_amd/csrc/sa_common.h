@@ -117,6 +117,9 @@ hipError_t launch_pack(const Dims& g, const int32_t* demand_ptr, const int32_t* 
 // Work queue (longest first, per-XCD ranges) and attention in one call; ws
 // holds attn_ws_bytes(g) bytes sized on the current device.
 size_t attn_ws_bytes(const Dims& g);
+// The work queue alone (whole items, never halves): what launch_attn needs
+// when given exactly this many workspace bytes.
+size_t attn_queue_ws_bytes(const Dims& g);
 int attn_workgroups(const Dims& g, int schedule);
 hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,

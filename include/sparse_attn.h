@@ -52,7 +52,9 @@ typedef enum sa_status {
   SA_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim/block/dtype mix  */
   SA_ERR_WORKSPACE = -3,    /* workspace smaller than sa_workspace_size       */
   SA_ERR_HIP = -4,          /* a HIP launch failed                            */
-  SA_ERR_CAPACITY = -5      /* demand union larger than the packed buffers    */
+  SA_ERR_CAPACITY = -5,     /* demand union larger than the packed buffers    */
+  SA_ERR_SCRATCH = -6       /* problem larger than the static scratch array of
+                               sparse_attn_forward_noalloc                    */
 } sa_status;
 
 typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -245,6 +247,27 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q,
                            const void* v_src, void* out, float* lse_opt, void* ws,
                            size_t ws_bytes, const sa_forward_opts* opts, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sparse_attn_forward without a workspace argument.  Its work queue lives in
+ * a file-scope device array of SA_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on every device it runs on until the process ends; the call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  It always processes whole items (never halves), so its results
+ * are bit-identical to sparse_attn_forward's whenever that call does not
+ * halve items, and otherwise equal up to the rounding of the halves'
+ * combination.  The queue needs 12 bytes per (head, query block) item plus
+ * 68 bytes; a problem needing more than SA_NOALLOC_SCRATCH_BYTES returns
+ * SA_ERR_SCRATCH before any HIP call.  Every call on a device shares that
+ * device's array (the queue kernel re-initialises what it reads), so calls
+ * that overlap in time on one device, from several streams or threads, race
+ * and must not be issued.  Other arguments as for sparse_attn_forward. */
+#define SA_NOALLOC_SCRATCH_BYTES (1u << 20)
+int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int32_t* row_ptr,
+                                const int32_t* col_idx, const int32_t* col_slot,
+                                const void* k_src, const void* v_src, void* out, float* lse_opt,
+                                void* stream);
+
 /* Gradients of sparse_attn_forward for an upstream gradient dout (the
  * training workload: the DSV explainer's speedups, "What it costs", are
  * training numbers).  With P = softmax(z) of the forward (same selected
@@ -313,9 +336,10 @@ int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 4 (1, plus the video block order entry points
+/* ABI version of this header: 5 (1, plus the video block order entry points
  * in 2, plus sparse_attn_backward in 3, plus sparse_attn_forward_ex and
- * sa_forward_workgroups in 4). */
+ * sa_forward_workgroups in 4, plus sparse_attn_forward_noalloc and
+ * SA_ERR_SCRATCH in 5). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 4
+    assert lib.sa_abi_version() == 5
 
 
 def test_struct_layout_matches_c():
@@ -58,7 +58,7 @@ def status_of_ws(prob, stage=B.SA_STAGE_SELECT):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(s)
     assert B.status_string(-99) == "unknown status"
 
@@ -270,3 +270,24 @@ def test_forward_workgroups_at_480p_geometry(lib):
     assert B.sa_forward_workgroups(p, B.SA_SCHEDULE_PER_UNIT) == 2 * 2808
     f32 = good_problem(dtype=B.SA_F32)
     assert B.sa_forward_workgroups(f32, B.SA_SCHEDULE_PERSISTENT) == 2 * 4
+
+
+def test_forward_noalloc_validation(lib):
+    """The no-alloc forward rejects bad arguments, and problems whose work
+    queue would not fit its static scratch array, before any HIP call."""
+    f = lib.sparse_attn_forward_noalloc
+    p = good_problem()
+    buf = ctypes.c_void_p(1 << 20)             # aligned, never dereferenced
+    args = [buf] * 7 + [None, None]
+    assert f(None, *args) == B.SA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), None, *args[1:]) == B.SA_ERR_INVALID_ARG
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert f(ctypes.byref(p), odd, *args[1:]) == B.SA_ERR_INVALID_ARG
+    bad = good_problem(head_dim=64)            # bf16 attention needs d = 128
+    assert f(ctypes.byref(bad), *args) == B.SA_ERR_UNSUPPORTED
+    # 1024 heads x 128 query blocks: 12 bytes per item no longer fit in 1 MiB
+    big = good_problem(heads=1024, q_rows=128 * 128, q_valid=128 * 128)
+    assert 12 * 1024 * 128 > B.SA_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), *args) == B.SA_ERR_SCRATCH
+    assert "scratch" in B.status_string(B.SA_ERR_SCRATCH)
+
