@@ -84,10 +84,12 @@ def load_traffic(config_name, nnz):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, n_items):
+def cpu_baseline(w, x, n_items, sa=None):
     """The oracle, as it stands, on a bounded sample: selection, CSR/demand/pack
     for every row (pro-rated by the item fraction) and dense masked attention
-    for ``n_items`` randomly chosen (head, query block) items."""
+    for ``n_items`` randomly chosen (head, query block) items.  With the GPU
+    path's buffers ``sa``, the oracle's results are also compared with the
+    GPU's (after the timing): returned as a ``parity`` entry."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import oracle as O
@@ -109,14 +111,17 @@ def cpu_baseline(w, x, n_items):
             s = O.block_scores_lowrank_mass(x["q"], x["k"], w.q_valid, w.kv_valid, w.block,
                                             x["wq"], x["wk"], w.eff_score_scale, items=items)
         mask = np.zeros(s.shape, bool)
+        recs = {}
         for h, i in items:
             rec = (O.select_row_top_p(s[h, i], w.top_p, w.top_k) if w.select_mode == 0
                    else O.select_row_top_k(s[h, i], w.top_k))
             mask[h, i, rec.order[:rec.m]] = True
+            recs[(h, i)] = rec
     else:
         _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
                                w.eff_score_scale, x.get("wq"), x.get("wk"))
-        mask, _ = O.select(s, w.select_mode, w.top_p, w.top_k)
+        mask, rec_list = O.select(s, w.select_mode, w.top_p, w.top_k)
+        recs = {(r // w.n_qb, r % w.n_qb): rec for r, rec in enumerate(rec_list)}
     rp, ci = O.csr(mask)
     dp, di, _, _ = O.demand(mask, rp, ci)
     O.pack(x["k"], dp, di, w.block)
@@ -124,19 +129,81 @@ def cpu_baseline(w, x, n_items):
     t_sel = time.perf_counter() - t0
     sel_rows = n_items if token else rows
     t0 = time.perf_counter()
-    O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block, w.eff_sm_scale,
-                items=items)
+    o_ref, lse_ref = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
+                                 w.eff_sm_scale, items=items)
     t_att = time.perf_counter() - t0
     nnz_sample = int(sum(mask[h, i].sum() for h, i in items))
     t = t_att + t_sel * n_items / sel_rows
     flops = 4.0 * w.block * w.block * w.head_dim * nnz_sample
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    parity = (parity_report(w, x, sa, mask, recs, items, o_ref, lse_ref)
+              if sa is not None else None)
+    return parity, {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"{n_items} of {rows} (head, query-block) items of {w.name}: dense fp32 "
                        f"masked attention for the sample ({t_att:.2f} s) + fp64 selection, CSR, "
                        f"demand and pack of " + ("the sampled rows" if token else "all rows") +
                        f" ({t_sel:.2f} s) pro-rated by {n_items}/{sel_rows}"),
             "seconds": round(t_att + t_sel, 3), "host_cpus": os.cpu_count()}
+
+
+def parity_report(w, x, sa, mask_ref, recs, items, o_ref, lse_ref):
+    """The GPU path's outputs of the timed run against the oracle's results of
+    the cpu_baseline leg (untimed):
+      - selection: every row the oracle selected (all rows, or the sampled
+        rows of the token-level modes); a differing row is excused only by the
+        oracle's near-tie rule at relative 1e-6 and counted, any other is
+        counted as a mismatch;
+      - CSR, demand set and slot map: bit-exact given the GPU's mask (every row);
+      - attention: max-abs error of the output and the LSE on the sampled items
+        (where a row was excused the oracle recomputes it on the GPU's mask);
+      - structure: selected fraction per head (min / mean / max over heads) and
+        the demand fraction (demanded blocks over H * nKB)."""
+    import numpy as np
+    from oracle import oracle as O
+    H, nqb, nkb = w.heads, w.n_qb, w.n_kb
+    gmask = O.bits_to_mask(sa.mask_bits.cpu().numpy().view(np.uint32), H, nqb, nkb)
+    excused = mismatched = 0
+    for (h, i), rec in recs.items():
+        if not np.array_equal(mask_ref[h, i], gmask[h, i]):
+            if O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, gmask[h, i], rel=1e-6):
+                excused += 1
+            else:
+                mismatched += 1
+    grp, gci = sa.host_csr()
+    orp, oci = O.csr(gmask)
+    odp, odi, _, ocs = O.demand(gmask, orp, oci)
+    total = int(odp[-1])
+    csr_exact = bool(np.array_equal(grp, orp) and np.array_equal(gci, oci))
+    demand_exact = bool(np.array_equal(sa.demand_ptr.cpu().numpy(), odp) and
+                        np.array_equal(sa.demand_idx[:total].cpu().numpy(), odi) and
+                        np.array_equal(sa.col_slot[:orp[-1]].cpu().numpy(), ocs))
+    redo = [(h, i) for h, i in items if not np.array_equal(mask_ref[h, i], gmask[h, i])]
+    if redo:
+        o2, l2 = O.attention(x["q"], x["k"], x["v"], gmask, w.q_valid, w.kv_valid, w.block,
+                             w.eff_sm_scale, items=redo)
+        for h, i in redo:
+            sl = slice(i * w.block, (i + 1) * w.block)
+            o_ref[h, sl], lse_ref[h, sl] = o2[h, sl], l2[h, sl]
+    go = sa.out.float().cpu().numpy()
+    gl = sa.lse.cpu().numpy()
+    err_o = err_l = 0.0
+    for h, i in items:
+        sl = slice(i * w.block, (i + 1) * w.block)
+        err_o = max(err_o, float(np.max(np.abs(go[h, sl] - o_ref[h, sl]))))
+        fin = np.isfinite(lse_ref[h, sl])
+        if fin.any():
+            err_l = max(err_l, float(np.max(np.abs(gl[h, sl][fin] - lse_ref[h, sl][fin]))))
+    frac = gmask.mean(axis=(1, 2))
+    return {"selection_rows_checked": len(recs), "near_tie_rows_excused": excused,
+            "selection_rows_mismatched": mismatched, "near_tie_rel": 1e-6,
+            "csr_bit_exact": csr_exact, "demand_and_slots_bit_exact": demand_exact,
+            "attention_items_checked": len(items),
+            "attention_max_abs_err": round(err_o, 6), "lse_max_abs_err": round(err_l, 6),
+            "attention_tol": 2e-2 if w.dtype == "bf16" else 1e-5,
+            "per_head_selected_fraction": {"min": round(float(frac.min()), 4),
+                                           "mean": round(float(frac.mean()), 4),
+                                           "max": round(float(frac.max()), 4)},
+            "demand_fraction": round(total / (H * nkb), 4)}
 
 
 def main():
@@ -297,7 +364,8 @@ def main():
         rec["load_balance"] = load_balance(sa, packed, flush)
         rec["dense_context"] = dense_context(w, d, sa, flush, packed, flops)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items)
+        parity, rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items, sa)
+        rec["parity"] = parity
     print(json.dumps(rec), flush=True)
 
 

@@ -1,10 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (select -> pack -> forward on packed K/V).
 
-Selection, CSR, demand sets, slot maps and packed buffers are checked on every
-row; attention on sampled (head, query block) items that the oracle computes
-one by one (first, last with the ragged query tail, heaviest, lightest and a
-few random ones), plus properties that hold everywhere (padded query rows are
+Selection, CSR, demand sets, slot maps, packed buffers and the work-unit order
+are checked on every row; attention on every (head, query block) item of the
+480p workload, and on sampled items of the others that the oracle computes one
+by one (first, last with the ragged query tail, heaviest, lightest and a few
+random ones), plus properties that hold everywhere (padded query rows are
 0 / -inf, every output row is finite)."""
 import numpy as np
 import pytest
@@ -64,7 +65,11 @@ def test_full_size_workload(name):
     del ref
     check_queue(w, sa)
 
-    items = sampled_items(w, orp)
+    # 480p, the headline workload: every (head, query block) item (about 45 s of
+    # host work on 16 threads); the others on sampled items
+    every = name == "480p"
+    items = ([(h, i) for h in range(w.heads) for i in range(w.n_qb)] if every
+             else sampled_items(w, orp))
     o, lse = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
                          w.eff_sm_scale, items=items)
     go = sa.out.float().cpu().numpy()
@@ -78,7 +83,8 @@ def test_full_size_workload(name):
         fin = np.isfinite(lse[h, sl])
         np.testing.assert_array_equal(np.isfinite(gl[h, sl]), fin)
         assert np.max(np.abs(gl[h, sl][fin] - lse[h, sl][fin])) <= TOL_LSE[w.dtype]
-    say(f"  attention on {len(items)} sampled items: max_abs_err={worst:.3g}")
+    say(f"  attention on {len(items)} {'(every)' if every else 'sampled'} items: "
+        f"max_abs_err={worst:.3g}")
     # everywhere: finite outputs, padded query rows are 0 / -inf
     assert np.all(np.isfinite(go))
     assert np.all(go[:, w.q_valid:] == 0) and np.all(np.isneginf(gl[:, w.q_valid:]))
