@@ -99,6 +99,9 @@ def cpu_baseline(w, x, n_items, sa=None):
     # and select the sampled rows only (CSR, demand and pack then cover
     # them), and sample fewer rows so the leg stays near 15 s
     token = w.score_mode in (2, 3)
+    # an item's dense masked attention costs in proportion to the key count:
+    # the default 768 items are sized for 32k keys
+    n_items = max(64, n_items * 32768 // max(w.kv_rows, 32768))
     n_items = min(n_items // 4 if token else n_items, rows)
     pick = np.random.default_rng(0).choice(rows, size=n_items, replace=False)
     items = [(int(r) // w.n_qb, int(r) % w.n_qb) for r in sorted(pick)]
@@ -363,6 +366,8 @@ def main():
     if w.dtype == "bf16" and not args.no_extras:
         rec["load_balance"] = load_balance(sa, packed, flush)
         rec["dense_context"] = dense_context(w, d, sa, flush, packed, flops)
+        if w.select_mode == 1 and w.score_mode in (0, 1) and not tiles:
+            rec["fused"] = fused_leg(w, d, sa, flush, args.steps, ms_step, flops)
     if not args.no_cpu_baseline:
         parity, rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items, sa)
         rec["parity"] = parity
@@ -460,6 +465,49 @@ def load_balance(sa, packed, flush, reps=5):
             "persistent_forward_ms": round(float(np.median(pers)), 4),
             "per_unit_workgroups": sa.workgroups(binding.SA_SCHEDULE_PER_UNIT),
             "per_unit_forward_ms": round(float(np.median(unit)), 4), "reps": reps}
+
+
+def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
+    """The fused single pass (sparse_attn_fused: pooling, then one kernel that
+    scores, keeps the top-k and attends per query block) timed like the step:
+    a flush, then the call, ``steps`` times; against the three-call path's ms
+    per layer of the timed steps.  Its kept sets are checked against the
+    three-call path's mask."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_scores_amd import binding
+    prob = sa.prob
+    n = binding.sa_workspace_size(prob, binding.SA_STAGE_FUSED)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(sa.out)
+    lse = torch.empty_like(sa.lse)
+    bits = torch.empty_like(sa.mask_bits)
+    lowrank = w.score_mode == 1
+
+    def run(mask=None):
+        binding.sparse_attn_fused(prob, sa.q, sa.k, sa.v, d.get("wq") if lowrank else None,
+                                  d.get("wk") if lowrank else None, out, lse, mask, ws, n)
+
+    run(bits)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(bits, sa.mask_bits))
+    ts = []
+    for r in range(steps):
+        _flush(flush, r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts = np.array(ts)
+    ms = float(np.median(ts))
+    return {"ms_per_layer": round(ms, 4),
+            "p10_p90": [round(float(np.percentile(ts, 10)), 4), round(float(np.percentile(ts, 90)), 4)],
+            "tflops": round(flops / (ms / 1e3) / 1e12, 3),
+            "three_call_ms_per_layer": round(three_call_ms, 4),
+            "speedup_over_three_call": round(three_call_ms / ms, 3),
+            "same_mask_as_three_call": same, "steps": steps}
 
 
 def dense_context(w, d, sa, flush, packed, flops, reps=5):

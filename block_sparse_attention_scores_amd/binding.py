@@ -29,12 +29,14 @@ SA_F32, SA_BF16 = 0, 1
 SA_TOP_P, SA_TOP_K = 0, 1
 SA_SCORE_POOLED, SA_SCORE_LOWRANK, SA_SCORE_LOWRANK_MAX, SA_SCORE_LOWRANK_MASS = 0, 1, 2, 3
 SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD, SA_STAGE_BACKWARD = 0, 1, 2, 3, 4
+SA_STAGE_FUSED = 5
 SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT = 0, 1
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
            "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
-           "sparse_attn_forward_ex", "sparse_attn_forward_noalloc", "sparse_attn_backward",
-           "sa_video_block_order", "sa_permute_rows", "sa_status_string", "sa_abi_version")
+           "sparse_attn_forward_ex", "sparse_attn_fused", "sparse_attn_forward_noalloc",
+           "sparse_attn_backward", "sa_video_block_order", "sa_permute_rows", "sa_status_string",
+           "sa_abi_version")
 
 
 class SaProblem(ctypes.Structure):
@@ -98,6 +100,7 @@ def load(path: str = None):
     lib.sa_forward_workgroups.argtypes = [prob, i32, ctypes.POINTER(i32)]
     lib.sparse_attn_forward_ex.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz,
                                            ctypes.POINTER(SaForwardOpts), P]
+    lib.sparse_attn_fused.argtypes = [prob, P, P, P, P, P, P, P, P, P, sz, P]
     lib.sparse_attn_forward_noalloc.argtypes = [prob, P, P, P, P, P, P, P, P, P]
     lib.sparse_attn_backward.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.sa_video_block_order.argtypes = [ctypes.POINTER(SaVideoTiling), i64, i64, P, P, P, P, P]
@@ -107,8 +110,9 @@ def load(path: str = None):
     lib.sa_abi_version.argtypes = []
     for name in ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
                  "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",
-                 "sparse_attn_forward_ex", "sparse_attn_forward_noalloc", "sparse_attn_backward",
-                 "sa_video_block_order", "sa_permute_rows", "sa_abi_version"):
+                 "sparse_attn_forward_ex", "sparse_attn_fused", "sparse_attn_forward_noalloc",
+                 "sparse_attn_backward", "sa_video_block_order", "sa_permute_rows",
+                 "sa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +203,13 @@ def sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, ou
         ctypes.byref(prob), _ptr(q), _ptr(row_ptr), _ptr(col_idx), _ptr(col_slot), _ptr(k_src),
         _ptr(v_src), _ptr(out), _ptr(lse_opt), _ptr(ws), ws_bytes, ctypes.byref(opts),
         _stream(stream)))
+
+
+def sparse_attn_fused(prob, q, k, v, wq, wk, out, lse_opt, mask_bits_opt, ws, ws_bytes,
+                      stream=None):
+    _check("sparse_attn_fused", load().sparse_attn_fused(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(out),
+        _ptr(lse_opt), _ptr(mask_bits_opt), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def sparse_attn_forward_noalloc(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt,

@@ -127,8 +127,15 @@ BackwardWs backward_ws(const Dims& g) {
   return w;
 }
 
+// The fused pass needs the select stage's block means and projections only:
+// the head of the select layout, up to the end of the key projections.
+size_t fused_ws(const Dims& g) {
+  return select_ws(g).kt + round_up(sizeof(double) * g.H * g.nkb * g.rank);
+}
+
 size_t stage_bytes(const Dims& g, int stage) {
   switch (stage) {
+    case SA_STAGE_FUSED: return fused_ws(g);
     case SA_STAGE_SELECT: return select_ws(g).total;
     case SA_STAGE_CSR: return csr_ws(g);
     case SA_STAGE_PACK: return pack_ws(g).total;
@@ -190,7 +197,7 @@ int check_forward_args(const Dims& g, const void* q, const int32_t* row_ptr,
 
 extern "C" {
 
-int sa_abi_version(void) { return 5; }
+int sa_abi_version(void) { return 6; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -212,7 +219,7 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes) {
   if (!bytes) return SA_ERR_INVALID_ARG;
   const int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  if (stage < SA_STAGE_SELECT || stage > SA_STAGE_BACKWARD) return SA_ERR_INVALID_ARG;
+  if (stage < SA_STAGE_SELECT || stage > SA_STAGE_FUSED) return SA_ERR_INVALID_ARG;
   *bytes = stage_bytes(g, stage);
   return SA_OK;
 }
@@ -347,6 +354,41 @@ int sparse_attn_forward(const sa_problem* prob, const void* q, const int32_t* ro
                         void* stream) {
   return sparse_attn_forward_ex(prob, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt,
                                 ws, ws_bytes, nullptr, stream);
+}
+
+int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, const void* v,
+                      const float* wq, const float* wk, void* out, float* lse_opt,
+                      uint32_t* mask_bits_opt, void* ws, size_t ws_bytes, void* stream) {
+  Dims g;
+  int st = check_problem(prob, &g);
+  if (st != SA_OK) return st;
+  if (g.dtype != SA_BF16 || g.d != 128 || g.B != 128 || prob->select_mode != SA_TOP_K ||
+      (g.score_mode != SA_SCORE_POOLED && g.score_mode != SA_SCORE_LOWRANK))
+    return SA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return SA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SA_ERR_INVALID_ARG;
+  if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  if (mask_bits_opt && ((uintptr_t)mask_bits_opt & 3u)) return SA_ERR_INVALID_ARG;
+  if (g.score_mode == SA_SCORE_LOWRANK && (!wq || !wk)) return SA_ERR_INVALID_ARG;
+  st = check_ws(g, SA_STAGE_FUSED, ws, ws_bytes);
+  if (st != SA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SelectWs w = select_ws(g);
+  double* qbar = at<double>(ws, w.qbar);
+  double* kbar = at<double>(ws, w.kbar);
+  double* qt = at<double>(ws, w.qt);
+  double* kt = at<double>(ws, w.kt);
+  const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
+  SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
+  if (g.rank > 0) {
+    SA_TRY_HIP(sa::launch_fused_topk(g, qt, kt, g.rank, 1.0, prob->top_k, q, k, v, out, lse_opt,
+                                     mask_bits_opt, sm, s));
+  } else {
+    const double sc = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);
+    SA_TRY_HIP(sa::launch_fused_topk(g, qbar, kbar, g.d, sc, prob->top_k, q, k, v, out, lse_opt,
+                                     mask_bits_opt, sm, s));
+  }
+  return SA_OK;
 }
 
 int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int32_t* row_ptr,

@@ -28,7 +28,7 @@
 
 #include <algorithm>
 
-#include "mfma_bf16.h"
+#include "attend_bf16.h"
 
 namespace sa {
 namespace {
@@ -285,17 +285,10 @@ __global__ __launch_bounds__(BLK) void attn_f32_kernel(
 // ---------------------------------------------------------------------------
 // bf16 MFMA path, d = 128, block = 128
 // ---------------------------------------------------------------------------
-// One (head, query block) item by one workgroup of four waves.  Per key block:
-//   S phase      S^T = K Q^T on MFMA (K from LDS, Q in registers)
-//   barrier      (all waves done with K; this wave's V loads have landed)
-//   K loads      the next block's K goes into LDS
-//   softmax, PV  O^T += V^T P^T (V from LDS through transposing reads)
-//   barrier      (all waves done with V; the next K has landed)
-//   V loads      the next block's V goes into LDS
-//
-// A halved item (one of two units of its list) ends by publishing its
-// unnormalised partial state, or, when the other half is already published,
-// by combining the two and writing the output (combine_halves).
+// One (head, query block) item, or one half of its block list, by one
+// workgroup of four waves (attend_blocks in attend_bf16.h).  A halved item
+// ends by publishing its unnormalised partial state, or, when the other half
+// is already published, by combining the two and writing the output.
 constexpr int kPartO = 16 * 256 * 4;              // fp32 O of the 256 lanes
 constexpr int kSlotFloats = kPartO + 2 * 256;     // + running max and sum per lane
 
@@ -308,173 +301,15 @@ __device__ __forceinline__ void attend_item(
     int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_valid, float scale_log2) {
   const int item = unit >> 1, part = unit & 1;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
   const int h = item / nqb, i = item % nqb;
-  const int qloc = 32 * wave + lq;                                // query row within the block
-
-  // lane offsets of the block loads (see dma_block): row 4i + L/16, chunk L%16
-  int kvo[4], vvo[4];
-  {
-    const int rr = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      kvo[p] = rr * 256 + ((pc ^ (4 * p + rr)) << 4);
-      vvo[p] = rr * 256 + ((pc ^ (4 * rr)) << 4);
-    }
-  }
-  // K operand reads: row 32t + lq, logical chunk 2s + g -> chunk (2s + g) ^ (lq & 15)
-  int ka[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) ka[s] = lq * 256 + (((2 * s + g) ^ (lq & 15)) << 4);
-  // V operand reads (transposing): lane j of 16-lane group a reads row
-  // 4 kga + e, columns 32u + 16 (a & 1) + 4 q .. +3, with e = j / 4, q = j % 4
-  int va[4];
-  {
-    const int a = lane >> 4, j = lane & 15, e = j >> 2, qq = j & 3;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      va[u] = 1024 * g + 256 * e + 64 * (u ^ e) + 32 * (a & 1) + 8 * qq;
-  }
-
-  // Q fragments (B operand of S^T = K Q^T): d = 16s + 8g .. +8
-  bf16x8 qf[8];
-  {
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(q + ((int64_t)h * q_rows + (int64_t)i * kB) * kD, kTileBytes);
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, qloc * 256 + 16 * g, 32 * s));
-  }
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[u][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
   // every value below is uniform across the workgroup; readfirstlane keeps it
   // in scalar registers (buffer descriptors need them)
   const Range range = unit_range(row_ptr, item, part, split);
   const int e0 = __builtin_amdgcn_readfirstlane(range.lo);
   const int e1 = __builtin_amdgcn_readfirstlane(range.hi);
-  // source block of entry e (-1: skip)
-  auto block_of = [&](int e) -> int64_t {
-    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
-    if ((unsigned)j >= (unsigned)nkb) return -1;
-    return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(col_slot[e]) : (int64_t)h * nkb + j;
-  };
-
-  int e = e0;
-  int64_t blk = -1;
-  while (e < e1 && (blk = block_of(e)) < 0) ++e;
-  if (e < e1) {
-    dma_block(k + blk * (kB * kD), kl, wave, kvo);
-    dma_block(v + blk * (kB * kD), vl, wave, vvo);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  while (e < e1) {
-    const int j = __builtin_amdgcn_readfirstlane(col_idx[e]);
-    int en = e + 1;
-    int64_t bn = -1;
-    while (en < e1 && (bn = block_of(en)) < 0) ++en;
-
-    // S^T tile t: keys 32t.., this lane's query; reg r -> key 32t + 8(r/4) + 4g + r%4
-    f32x16 sacc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            reinterpret_cast<const char*>(kl) + ka[s] + t * 8192);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
-      }
-
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
-    __syncthreads();
-    if (en < e1) dma_block(k + bn * (kB * kD), kl, wave, kvo);
-
-    // valid keys of this block (uniform); only the sequence's last block is ragged
-    const int lim = __builtin_amdgcn_readfirstlane((int)min((int64_t)kB, kv_valid - (int64_t)j * kB));
-    float mx = -INFINITY;
-    if (__builtin_expect(lim < kB, 0)) {
-      const int lim_g = lim - 4 * g;   // key 32t + 8(r/4) + 4g + r%4 >= lim
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + (r & 3) >= lim_g) sacc[t][r] = -INFINITY;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-    // The running max only moves when some query's block max exceeds it by
-    // more than 8 (log2 units): until then P = exp2(S*scale - m) stays below
-    // 2^8, and softmax does not depend on which reference max is used.  Most
-    // rescales of O are skipped (wave-uniform branch).
-    if (__ballot(mx > m_run + 8.f)) {
-      const float mn = fmaxf(m_run, mx);
-      // v_exp_f32 directly: masses below 2^-126 flush to 0, which softmax tolerates
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[u][r] *= alpha;
-      l_run *= alpha;
-      m_run = mn;
-    }
-    const float mn = m_run;
-    // Raised wave priority for the softmax and P V phase, where exponentials
-    // and MFMAs alternate: the other workgroup's wave on this SIMD, when it is
-    // in its score MFMAs, fills the slots this one leaves (measured 0.5-1%
-    // faster than raising the score phase instead).
-    __builtin_amdgcn_s_setprio(1);
-
-    // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
-    // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
-    // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g (the transposing reads
-    // at rows 4 kga + e and 4 (kga + 2) + e).  The exp of tile t+1 is
-    // independent of the MFMAs of tile t, so the two can overlap.
-    float ps = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -mn));
-        sacc[t][r] = p;
-        ps += p;
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
-        const int rows = 1024 * (8 * t + 4 * h2);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x2 lo = lds_read_tr(vl, va[u] + rows);
-          const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
-          const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
-                                                            oacc[u], 0, 0, 0);
-        }
-      }
-    }
-    l_run += ps;
-    __builtin_amdgcn_s_setprio(0);
-
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's K loads of the next block
-    __syncthreads();
-    if (en < e1) dma_block(v + bn * (kB * kD), vl, wave, vvo);
-    e = en;
-  }
+  AttnState st;
+  attend_blocks(st, CsrBlockList{col_idx, col_slot, h, nkb}, e0, e1, kl, vl, q, k, v, h, i,
+                q_rows, kv_valid, scale_log2);
 
   if (range.halved) {
     // Partial state of this half, lane-major so that each store instruction
@@ -493,9 +328,10 @@ __device__ __forceinline__ void attend_item(
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
           reinterpret_cast<float4*>(mine)[(4 * u + r4) * 256 + tid] =
-              make_float4(oacc[u][4 * r4], oacc[u][4 * r4 + 1], oacc[u][4 * r4 + 2], oacc[u][4 * r4 + 3]);
-      mine[kPartO + tid] = m_run;
-      mine[kPartO + 256 + tid] = l_run;
+              make_float4(st.oacc[u][4 * r4], st.oacc[u][4 * r4 + 1], st.oacc[u][4 * r4 + 2],
+                          st.oacc[u][4 * r4 + 3]);
+      mine[kPartO + tid] = st.m_run;
+      mine[kPartO + 256 + tid] = st.l_run;
       __threadfence();
       __syncthreads();
       if (tid == 0) *flag = atomicAdd(&done[item], 1);
@@ -508,8 +344,8 @@ __device__ __forceinline__ void attend_item(
     // depend on which half finished first: with M = max(m0, m1),
     //   O = O1 * 2^(m1 - M) + O0 * 2^(m0 - M),  l likewise.
     const float m_o = other[kPartO + tid], l_o = other[kPartO + 256 + tid];
-    const float m0 = part ? m_o : m_run, m1 = part ? m_run : m_o;
-    const float l0 = part ? l_o : l_run, l1 = part ? l_run : l_o;
+    const float m0 = part ? m_o : st.m_run, m1 = part ? st.m_run : m_o;
+    const float l0 = part ? l_o : st.l_run, l1 = part ? st.l_run : l_o;
     const float mm = fmaxf(m0, m1);
     const bool any = mm > -INFINITY;
     const float a0 = any ? __builtin_amdgcn_exp2f(m0 - mm) : 0.f;
@@ -522,33 +358,15 @@ __device__ __forceinline__ void attend_item(
         const float ov[4] = {ot.x, ot.y, ot.z, ot.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float own = oacc[u][4 * r4 + x];
+          const float own = st.oacc[u][4 * r4 + x];
           const float v0 = part ? ov[x] : own, v1 = part ? own : ov[x];
-          oacc[u][4 * r4 + x] = fmaf(v1, a1, v0 * a0);
+          st.oacc[u][4 * r4 + x] = fmaf(v1, a1, v0 * a0);
         }
       }
-    l_run = fmaf(l1, a1, l0 * a0);
-    m_run = mm;
+    st.l_run = fmaf(l1, a1, l0 * a0);
+    st.m_run = mm;
   }
-
-  // finalise: O[query][d], reg r of d-tile u -> d = 32u + 8(r/4) + 4g + r%4
-  const int64_t qrow = (int64_t)i * kB + qloc;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool live = qrow < q_valid && l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
-  uint16_t* op = out + ((int64_t)h * q_rows + qrow) * kD;
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 o4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) o4[x] = oacc[u][4 * r4 + x] * inv;
-      *reinterpret_cast<bf16x4*>(op + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(o4, bf16x4);
-    }
-  if (lse && g == 0)
-    lse[(int64_t)h * q_rows + qrow] =
-        live ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  store_rows(st, out, lse, h, i, q_rows, q_valid);
 }
 
 // Persistent (max_units unbounded): each workgroup pops units from its XCD's

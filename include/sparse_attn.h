@@ -72,7 +72,8 @@ typedef enum sa_stage {
   SA_STAGE_CSR = 1,      /* sparse_attn_csr_from_mask  */
   SA_STAGE_PACK = 2,     /* kv_demand_pack             */
   SA_STAGE_FORWARD = 3,  /* sparse_attn_forward        */
-  SA_STAGE_BACKWARD = 4  /* sparse_attn_backward       */
+  SA_STAGE_BACKWARD = 4, /* sparse_attn_backward       */
+  SA_STAGE_FUSED = 5     /* sparse_attn_fused          */
 } sa_stage;
 
 /* Problem description (host struct, read during the call only).
@@ -247,6 +248,33 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q,
                            const void* v_src, void* out, float* lse_opt, void* ws,
                            size_t ws_bytes, const sa_forward_opts* opts, void* stream);
 
+/* Critical-KV estimation and sparse attention in one pass (DSV explainer,
+ * "The idea": kernels that fuse the estimation of the critical keys and
+ * values with the sparse attention, keep intermediates on chip and never
+ * build the full score matrix).  The same result as sparse_attn_select with
+ * SA_TOP_K followed by sparse_attn_forward on the full K and V, but after the
+ * pooling pass (block means, and their rank-r projections in
+ * SA_SCORE_LOWRANK) a single kernel scores each query block against every key
+ * block of its head, keeps the min(top_k, nKB) largest scores (ties to the
+ * lower block id) and attends to them; no score matrix, mask or CSR goes to
+ * memory.
+ *   Supported: bf16, head_dim = block = 128, select_mode SA_TOP_K,
+ *   score_mode SA_SCORE_POOLED or SA_SCORE_LOWRANK (rank <= 64); else
+ *   SA_ERR_UNSUPPORTED.  Scores are fp64 (each a sequential fused
+ *   multiply-add over the pooled dimension), so the kept sets equal
+ *   sparse_attn_select's except where two scores tie to fp64 rounding.
+ * q [H,q_rows,d], k, v [H,kv_rows,d]: bf16; wq, wk: fp32 [H,d,rank] in
+ *   SA_SCORE_LOWRANK (else ignored, may be NULL);
+ * out [H,q_rows,d] bf16, lse_opt NULL or fp32 [H,q_rows]: as for
+ *   sparse_attn_forward;
+ * mask_bits_opt: NULL, or out uint32 [H*nQB, W] (the kept sets, laid out as
+ *   sparse_attn_select writes them), for checking;
+ * ws: workspace of sa_workspace_size(SA_STAGE_FUSED) bytes (the block means
+ *   and projections). */
+int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, const void* v,
+                      const float* wq, const float* wk, void* out, float* lse_opt,
+                      uint32_t* mask_bits_opt, void* ws, size_t ws_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * sparse_attn_forward without a workspace argument.  Its work queue lives in
@@ -336,10 +364,10 @@ int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 5 (1, plus the video block order entry points
+/* ABI version of this header: 6 (1, plus the video block order entry points
  * in 2, plus sparse_attn_backward in 3, plus sparse_attn_forward_ex and
  * sa_forward_workgroups in 4, plus sparse_attn_forward_noalloc and
- * SA_ERR_SCRATCH in 5). */
+ * SA_ERR_SCRATCH in 5, plus sparse_attn_fused and SA_STAGE_FUSED in 6). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

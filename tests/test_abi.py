@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 5
+    assert lib.sa_abi_version() == 6
 
 
 def test_struct_layout_matches_c():
@@ -291,3 +291,29 @@ def test_forward_noalloc_validation(lib):
     assert f(ctypes.byref(big), *args) == B.SA_ERR_SCRATCH
     assert "scratch" in B.status_string(B.SA_ERR_SCRATCH)
 
+
+def test_fused_validation(lib):
+    """sparse_attn_fused: only bf16, d = B = 128, fixed top-k over pooled or
+    rank-r scores; argument and workspace errors before any HIP call."""
+    f = lib.sparse_attn_fused
+    buf = ctypes.c_void_p(1 << 20)
+    ok = good_problem(select_mode=B.SA_TOP_K, top_k=3, score_mode=B.SA_SCORE_LOWRANK, rank=16)
+    st, need = status_of_ws(ok, B.SA_STAGE_FUSED)
+    assert st == 0 and need > 0 and need % 256 == 0
+    # block means of Q and K plus their rank-16 projections, fp64
+    H, nqb, nkb, d = 2, 4, 8, 128
+    assert need >= 8 * (H * nqb * d + H * nkb * d + H * (nqb + nkb) * 16)
+    ws = ctypes.c_void_p(1 << 24)
+
+    def call(p, q=buf, wq=buf, ws_=ws, n=need):
+        return f(ctypes.byref(p), q, buf, buf, wq, buf, buf, None, None, ws_, n, None)
+
+    assert call(good_problem()) == B.SA_ERR_UNSUPPORTED                     # top-p
+    assert call(good_problem(select_mode=B.SA_TOP_K, dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
+    assert call(good_problem(select_mode=B.SA_TOP_K, head_dim=64)) == B.SA_ERR_UNSUPPORTED
+    assert call(good_problem(select_mode=B.SA_TOP_K, score_mode=B.SA_SCORE_LOWRANK_MAX)) == \
+        B.SA_ERR_UNSUPPORTED
+    assert call(ok, q=None) == B.SA_ERR_INVALID_ARG
+    assert call(ok, wq=None) == B.SA_ERR_INVALID_ARG                      # low-rank needs W
+    assert call(ok, n=need - 256) == B.SA_ERR_WORKSPACE
+    assert call(ok, ws_=ctypes.c_void_p((1 << 24) + 64)) == B.SA_ERR_INVALID_ARG

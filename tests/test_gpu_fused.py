@@ -1,0 +1,147 @@
+"""GPU parity of the fused single pass (sparse_attn_fused: estimation, top-k
+and attention in one kernel per query block) through the C ABI.
+
+Bars: the kept sets equal the oracle's top-k on every row except near-ties
+(relative 1e-6 of the row's largest |score|, counted); every row keeps exactly
+min(k, nKB) blocks; attention max-abs error <= 2e-2 against the oracle's dense
+fp32 attention under the fused pass's own mask; and, where the three-call path
+(sparse_attn_select -> sparse_attn_forward on the full K/V) keeps the same
+blocks and does not halve items, the outputs of the two are equal bit for bit
+(the same attention core over the same ascending block lists)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from block_sparse_attention_scores_amd import binding as B
+from block_sparse_attention_scores_amd import inputs as I
+from block_sparse_attention_scores_amd.path import SparseAttention, problem_for, to_device
+
+from test_gpu_parity import TOL_LSE, TOL_OUT, items_split, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def fused(w, d):
+    prob = problem_for(w)
+    W = (w.n_kb + 31) // 32
+    out = torch.full_like(d["q"], float("nan"))
+    lse = torch.full((w.heads, w.q_rows), float("nan"), dtype=torch.float32, device="cuda")
+    bits = torch.full((w.heads * w.n_qb, W), -1, dtype=torch.int32, device="cuda")
+    n = B.sa_workspace_size(prob, B.SA_STAGE_FUSED)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    lowrank = w.score_mode == I.SCORE_LOWRANK
+    B.sparse_attn_fused(prob, d["q"], d["k"], d["v"], d["wq"] if lowrank else None,
+                        d["wk"] if lowrank else None, out, lse, bits, ws, n)
+    torch.cuda.synchronize()
+    return out, lse, bits
+
+
+def check_fused(w, items=None, compare_three_call=True):
+    say("case", w.name, "heads", w.heads, "nqb", w.n_qb, "nkb", w.n_kb, "k", w.top_k)
+    x = I.generate(w)
+    d = to_device(x, w)
+    out, lse, bits = fused(w, d)
+    mask = O.bits_to_mask(bits.cpu().numpy().view(np.uint32), w.heads, w.n_qb, w.n_kb)
+    if w.n_kb % 32:
+        assert np.all(bits.cpu().numpy().view(np.uint32)[:, -1] >> np.uint32(w.n_kb % 32) == 0)
+    assert np.all(mask.sum(axis=2) == min(w.top_k, w.n_kb))
+    _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
+                           w.eff_score_scale, x.get("wq"), x.get("wk"))
+    excused = 0
+    for h in range(w.heads):
+        for i in range(w.n_qb):
+            rec = O.select_row_top_k(s[h, i], w.top_k)
+            want = np.zeros(w.n_kb, bool)
+            want[rec.order[:rec.m]] = True
+            if not np.array_equal(want, mask[h, i]):
+                assert O.row_mismatch_excused(rec, I.SELECT_TOP_K, w.top_p, w.top_k, mask[h, i],
+                                              rel=1e-6), (h, i)
+                excused += 1
+    todo = items if items is not None else [(h, i) for h in range(w.heads) for i in range(w.n_qb)]
+    o, l = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
+                       w.eff_sm_scale, items=todo)
+    go, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for h, i in todo:
+        sl = slice(i * w.block, (i + 1) * w.block)
+        err = float(np.max(np.abs(go[h, sl] - o[h, sl])))
+        worst = max(worst, err)
+        assert err <= TOL_OUT["bf16"], (h, i, err)
+        fin = np.isfinite(l[h, sl])
+        np.testing.assert_array_equal(np.isfinite(gl[h, sl]), fin)
+        assert np.max(np.abs(gl[h, sl][fin] - l[h, sl][fin])) <= TOL_LSE["bf16"]
+    # padded query rows: exactly 0 / -inf, everywhere
+    assert np.all(go[:, w.q_valid:] == 0) and np.all(np.isneginf(gl[:, w.q_valid:]))
+    assert np.all(np.isfinite(go))
+    same = None
+    if compare_three_call:
+        sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
+        sa.select()
+        sa.forward(packed=False)
+        torch.cuda.synchronize()
+        same = torch.equal(sa.mask_bits, bits)
+        if same and not items_split(w):
+            assert torch.equal(sa.out, out) and torch.equal(sa.lse, lse)
+        elif same:
+            assert float((sa.out.float() - out.float()).abs().max()) <= TOL_OUT["bf16"]
+    say(f"  excused={excused} attention items={len(todo)} max_abs_err={worst:.3g} "
+        f"same mask as three-call: {same}")
+    return mask
+
+
+def lowrank_small(**kw):
+    base = dict(name="fused_lowrank", heads=2, head_dim=128, block=128, dtype="bf16",
+                latent=(4, 16, 37), q_start=0, q_valid=700, seed=91, strength=2.0,
+                tile=(2, 4, 4), clusters=6, select_mode=I.SELECT_TOP_K, top_k=5,
+                score_mode=I.SCORE_LOWRANK)
+    base.update(kw)
+    return I.Workload(**base)
+
+
+def test_fused_lowrank_ragged_tails():
+    w = lowrank_small()
+    assert w.kv_valid % w.block and w.q_valid % w.block
+    check_fused(w)
+
+
+def test_fused_pooled_top_k_two_mask_words():
+    w = lowrank_small(name="fused_pooled", latent=(4, 30, 39), q_valid=1000, top_k=7,
+                      score_mode=I.SCORE_POOLED, score_scale=1.0, seed=92)
+    assert w.n_kb == 37
+    check_fused(w)
+
+
+@pytest.mark.parametrize("k", [1, 19, 50])
+def test_fused_k_one_and_k_at_or_above_nkb(k):
+    w = lowrank_small(name=f"fused_k{k}", top_k=k, seed=93)
+    assert w.n_kb == 19
+    mask = check_fused(w)
+    if k >= w.n_kb:
+        assert mask.all()
+
+
+def test_fused_4096_key_blocks():
+    """The largest key-block count: 16 keys per thread in the selection."""
+    w = lowrank_small(name="fused_4096", heads=1, latent=(1, 1, 4096 * 128 - 5), q_valid=300,
+                      tile=(1, 1, 512), clusters=8, top_k=200, seed=94)
+    assert w.n_kb == 4096
+    check_fused(w, items=[(0, 0), (0, 2)], compare_three_call=False)
+
+
+def test_fused_full_size_lowrank():
+    """The low-rank workload at full size: every row's kept set against the
+    oracle, attention on sampled items against the oracle, and every output
+    against the three-call path bit for bit (same masks, whole items)."""
+    w = I.named("lowrank")
+    rng = np.random.default_rng(0)
+    rows = w.heads * w.n_qb
+    pick = sorted({0, rows - 1} | set(rng.choice(rows, size=6, replace=False).tolist()))
+    check_fused(w, items=[(r // w.n_qb, r % w.n_qb) for r in pick])
