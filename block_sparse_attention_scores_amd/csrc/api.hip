@@ -88,12 +88,12 @@ SelectWs select_ws(const Dims& g) {
   w.qt = o; o += round_up(sizeof(double) * g.H * g.nqb * g.rank);
   w.kt = o; o += round_up(sizeof(double) * g.H * g.nkb * g.rank);
   const bool token = g.score_mode == SA_SCORE_LOWRANK_MAX || g.score_mode == SA_SCORE_LOWRANK_MASS;
-  const size_t tok = token ? 32 : 0;   // projected tokens: 16 bf16 hi + 16 bf16 lo
-  w.qtok = o; o += round_up(sizeof(uint16_t) * g.H * g.q_rows * tok);
-  w.ktok = o; o += round_up(sizeof(uint16_t) * g.H * g.kv_rows * tok);
+  const size_t tok = token ? 16 : 0;   // projected tokens: 16 fp64 components
+  w.qtok = o; o += round_up(sizeof(double) * g.H * g.q_rows * tok);
+  w.ktok = o; o += round_up(sizeof(double) * g.H * g.kv_rows * tok);
   // per query token and key block: ln of the predicted exp-sum (mass mode)
   const size_t lse_n = g.score_mode == SA_SCORE_LOWRANK_MASS ? (size_t)g.H * g.nkb * g.q_rows : 0;
-  w.lse = o; o += round_up(sizeof(float) * lse_n);
+  w.lse = o; o += round_up(sizeof(double) * lse_n);
   w.scores = o; o += round_up(sizeof(double) * g.H * g.nqb * g.nkb);
   w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nqb);
   w.total = o;
@@ -249,12 +249,12 @@ int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, con
 
   SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
   if (g.score_mode == SA_SCORE_LOWRANK_MAX) {
-    SA_TRY_HIP(sa::launch_lowrank_max(g, q, k, wq, wk, at<uint16_t>(ws, w.qtok),
-                                      at<uint16_t>(ws, w.ktok), scores, s));
+    SA_TRY_HIP(sa::launch_lowrank_max(g, q, k, wq, wk, at<double>(ws, w.qtok),
+                                      at<double>(ws, w.ktok), scores, s));
   } else if (g.score_mode == SA_SCORE_LOWRANK_MASS) {
-    const float tau = prob->score_scale > 0.f ? prob->score_scale : (float)(1.0 / sqrt((double)g.d));
-    SA_TRY_HIP(sa::launch_lowrank_mass(g, q, k, wq, wk, tau, at<uint16_t>(ws, w.qtok),
-                                       at<uint16_t>(ws, w.ktok), at<float>(ws, w.lse), scores, s));
+    const double tau = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);
+    SA_TRY_HIP(sa::launch_lowrank_mass(g, q, k, wq, wk, tau, at<double>(ws, w.qtok),
+                                       at<double>(ws, w.ktok), at<double>(ws, w.lse), scores, s));
   } else if (g.rank > 0) {
     SA_TRY_HIP(sa::launch_scores(g, qt, kt, g.rank, 1.0, scores, s));
   } else {

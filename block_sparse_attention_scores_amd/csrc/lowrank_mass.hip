@@ -13,125 +13,143 @@
 // so that a softmax over a row of S gives back the masses (each row of M sums
 // to one) and top-k keeps the largest masses.
 //
-//   (projections: launch_token_projection, fp64 sums rounded to fp32 and
-//    stored as bf16 hi + lo)
+//   (projections: launch_token_projection, fp64)
 //   block_lse_kernel   one workgroup per (head, query block, run of key
-//                      blocks); each wave forms S^T = K~ Q~^T for its 32 query
-//                      tokens against a key block (split-bf16 matrix-core
-//                      products, token_mma.h; keys as rows, so each lane
-//                      holds one query's scores),
-//                      masks keys past kv_valid, and writes L[a, j] (fp32,
-//                      layout [H, nKB, q_rows]: 32 consecutive queries per
-//                      store).
+//                      blocks); each key block's projections are staged in LDS
+//                      (double-buffered); each wave forms the fp64 scores of
+//                      its query tokens against the block's keys on the fp64
+//                      matrix cores (keys as rows, so a lane holds 4 keys of
+//                      one query per 16-key tile), masks keys past kv_valid
+//                      and writes L[a, j] in fp64 (layout [H, nKB, q_rows]).
+//                      Each exponential is 2^n * exp2(f) with n an integer and
+//                      f in [-1, 0] formed exactly in fp64, f rounded to fp32
+//                      (2^-25 absolute) and exp2 in fp32; the sums are fp64.
+//                      So L is within about 2^-23 of the exact value.
 //   block_mass_kernel  one workgroup per (head, query block): LSE_a over j by
-//                      one thread per query (online max and sum), then one
-//                      thread per key block sums exp(L - LSE) over the valid
-//                      queries in query order and writes S as fp64.
+//                      one thread per query (online max and sum, fp64), then
+//                      one thread per key block sums exp(L - LSE) over the
+//                      valid queries in query order (fp64) and writes S.
 #include <float.h>
 #include <math.h>
 
 #include <algorithm>
 
-#include "token_mma.h"
+#include "token_f64.h"
 
 namespace sa {
 namespace {
 
-constexpr int kTokWords = 32;   // bf16 hi and lo of the 16 components per token
+using token::kRank;
+using token::kRow;
 constexpr int kRunKB = 16;      // key blocks per workgroup in block_lse_kernel
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994530942f;
+constexpr double kLog2e = 1.4426950408889634074;
 
+// exp(x) for x <= 0 to about 2^-23 relative: x log2 e = n + f with n an
+// integer and f in [-1, 0] (exact up to the fp64 product), exp2(f) in fp32.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  const double y = x * kLog2e;
+  if (y < -1000.0) return 0.0;
+  const double n = ceil(y);
+  const float f = (float)(y - n);
+  return ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+}
+
+// B = 128: each wave owns two 16-token query tiles; B = 64: one.
 template <int B>
-__global__ __launch_bounds__(256, 2) void block_lse_kernel(const uint16_t* __restrict__ qt,
-                                                        const uint16_t* __restrict__ kt, int nkb,
+__global__ __launch_bounds__(256, 2) void block_lse_kernel(const double* __restrict__ qt,
+                                                        const double* __restrict__ kt, int nkb,
                                                         int64_t q_rows, int64_t kv_rows,
-                                                        int64_t kv_valid, float tau,
-                                                        float* __restrict__ L) {
-  constexpr int kTiles = B / 32;   // 32-key tiles per block
+                                                        int64_t kv_valid, double tau,
+                                                        double* __restrict__ L) {
+  constexpr int QT = B / 64, KT = B / 16;
+  __shared__ double ks[2][B * kRow];
   const int h = blockIdx.z, i = blockIdx.y, j0 = blockIdx.x * kRunKB;
-  const int wave = threadIdx.x / kWave, lane = lane_id(), g = lane >> 5, lr = lane & 31;
-  if (wave >= kTiles) return;   // B = 64: two waves hold the block's queries
+  const int wave = threadIdx.x / kWave, lane = lane_id(), g = lane >> 4, r = lane & 15;
   const int jn = min(kRunKB, nkb - j0);
-  const int64_t qrow = (int64_t)i * B + 32 * wave + lr;
-  // B operand: this lane's query, rank components 8g .. 8g+7
-  const token::Split bq = token::split_load(qt + ((int64_t)h * q_rows + qrow) * kTokWords, g);
-  const float tl = tau * kLog2e;   // logits in log2 units: z * log2(e) = tl * score
+  // B operands: this lane supplies query token 16 (QT wave + t) + r of the block
+  double bq[QT][4];
+#pragma unroll
+  for (int t = 0; t < QT; ++t)
+    token::operand_global(qt + ((int64_t)h * q_rows + (int64_t)i * B + 16 * (QT * wave + t) + r) * kRank,
+                          g, bq[t]);
+  const double* kh = kt + (int64_t)h * kv_rows * kRank;
+  token::stage(kh + (int64_t)j0 * B * kRank, ks[0], B);
+  __syncthreads();
   for (int jj = 0; jj < jn; ++jj) {
     const int j = j0 + jj;
-    const int64_t key0 = (int64_t)j * B;
+    if (jj + 1 < jn) token::stage(kh + (int64_t)(j + 1) * B * kRank, ks[(jj + 1) & 1], B);
+    const double* kb = ks[jj & 1];
     // valid keys of this block (uniform); only the last block is ragged
-    const int lim = (int)min<int64_t>(B, kv_valid - key0);
-    f32x16 acc[kTiles];
+    const int lim = (int)min<int64_t>(B, kv_valid - (int64_t)j * B);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const token::Split ak =
-          token::split_load(kt + ((int64_t)h * kv_rows + key0 + 32 * t + lr) * kTokWords, g);
-      acc[t] = token::scores(ak, bq);
+    for (int t = 0; t < QT; ++t) {
+      // tile u, element q: key 16u + 4q + g of the block, query r of tile t
+      token::f64x4 z[KT];
+#pragma unroll
+      for (int u = 0; u < KT; ++u) {
+        double a[4];
+        token::operand_lds(kb, 16 * u + r, g, a);
+        z[u] = token::tile(a, bq[t]);
+      }
+      double mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < KT; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (16 * u + 4 * q + g < lim) mx = fmax(mx, z[u][q]);
+      mx = fmax(mx, token::shfl_xor_f64(mx, 16));
+      mx = fmax(mx, token::shfl_xor_f64(mx, 32));
+      double sum = 0.0;
+#pragma unroll
+      for (int u = 0; u < KT; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (16 * u + 4 * q + g < lim) sum += exp_nonpos(tau * (z[u][q] - mx));
+      sum += token::shfl_xor_f64(sum, 16);
+      sum += token::shfl_xor_f64(sum, 32);
+      // every block holds a valid key, so mx is finite and sum >= 1
+      if (g == 0)
+        L[((int64_t)h * nkb + j) * q_rows + (int64_t)i * B + 16 * (QT * wave + t) + r] =
+            tau * mx + log(sum);
     }
-    // reg r of tile t: key 32t + 8(r/4) + 4g + r%4 of the block, this lane's query
-    if (__builtin_expect(lim < B, 0)) {
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) acc[t][r] = -INFINITY;
-    }
-    // max of the raw scores (tl > 0), then exp2(tl * s - tl * max) as one FMA
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float off = -mx * tl;
-    float sum = 0.f;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][r], tl, off));
-    sum += __shfl_xor(sum, 32, kWave);
-    // every block holds a valid key, so mx is finite and sum >= 1
-    if (g == 0) L[((int64_t)h * nkb + j) * q_rows + qrow] = (mx * tl + __log2f(sum)) * kLn2;
+    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(256) void block_mass_kernel(const float* __restrict__ L, int nqb,
+__global__ __launch_bounds__(256) void block_mass_kernel(const double* __restrict__ L, int nqb,
                                                          int nkb, int B, int64_t q_rows,
                                                          int64_t q_valid,
                                                          double* __restrict__ S) {
-  __shared__ float lse[128];
+  __shared__ double lse[128];
   const int h = blockIdx.y, i = blockIdx.x, t = threadIdx.x;
   const int64_t q0 = (int64_t)i * B;
   const int n_valid = (int)min<int64_t>(B, q_valid - q0);
-  const float* Lh = L + (int64_t)h * nkb * q_rows + q0;
+  const double* Lh = L + (int64_t)h * nkb * q_rows + q0;
   if (t < B) {
-    float m = -INFINITY, s = 0.f;
+    double m = -INFINITY, s = 0.0;
     if (t < n_valid) {
       for (int j = 0; j < nkb; ++j) {
-        const float v = Lh[(int64_t)j * q_rows + t];
+        const double v = Lh[(int64_t)j * q_rows + t];
         if (v > m) {
-          s = s * __expf(m - v) + 1.f;
+          s = s * exp(m - v) + 1.0;
           m = v;
         } else {
-          s += __expf(v - m);
+          s += exp(v - m);
         }
       }
     }
-    lse[t] = t < n_valid ? m + __logf(s) : INFINITY;   // +inf: the query adds nothing
+    lse[t] = t < n_valid ? m + log(s) : INFINITY;   // +inf: the query adds nothing
   }
   __syncthreads();
   for (int j = t; j < nkb; j += blockDim.x) {
-    const float4* row = reinterpret_cast<const float4*>(Lh + (int64_t)j * q_rows);
-    float acc = 0.f;
-    for (int c = 0; c < B / 4; ++c) {
-      const float4 v = row[c];
-      acc += __expf(v.x - lse[4 * c]);
-      acc += __expf(v.y - lse[4 * c + 1]);
-      acc += __expf(v.z - lse[4 * c + 2]);
-      acc += __expf(v.w - lse[4 * c + 3]);
+    const double2* row = reinterpret_cast<const double2*>(Lh + (int64_t)j * q_rows);
+    double acc = 0.0;
+    for (int c = 0; c < B / 2; ++c) {
+      const double2 v = row[c];
+      acc += exp(v.x - lse[2 * c]);
+      acc += exp(v.y - lse[2 * c + 1]);
     }
-    const double m = (double)acc / n_valid;
+    const double m = acc / n_valid;
     S[((int64_t)h * nqb + i) * nkb + j] = m > 0.0 ? log(m) : -INFINITY;
   }
 }
@@ -139,8 +157,8 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const float* __restrict
 }  // namespace
 
 hipError_t launch_lowrank_mass(const Dims& g, const void* q, const void* k, const float* wq,
-                               const float* wk, float tau, uint16_t* qtok, uint16_t* ktok,
-                               float* lbuf, double* scores, hipStream_t s) {
+                               const float* wk, double tau, double* qtok, double* ktok,
+                               double* lbuf, double* scores, hipStream_t s) {
   hipError_t e = launch_token_projection(g, q, k, wq, wk, qtok, ktok, s);
   if (e != hipSuccess) return e;
   const dim3 grid((g.nkb + kRunKB - 1) / kRunKB, g.nqb, g.H);

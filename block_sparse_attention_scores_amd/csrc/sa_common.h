@@ -142,14 +142,14 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
                            void* dv, float* delta, uint32_t* bits, int32_t* counts,
                            int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s);
-// Token projections for the token-level estimators: per token 16 fp32
-// components stored as 16 bf16 hi then 16 bf16 lo (64 bytes).
+// Token projections for the token-level estimators: per token the 16 fp64
+// components of x W (128 bytes).
 hipError_t launch_token_projection(const Dims& g, const void* q, const void* k, const float* wq,
-                                   const float* wk, uint16_t* qtok, uint16_t* ktok, hipStream_t s);
+                                   const float* wk, double* qtok, double* ktok, hipStream_t s);
 hipError_t launch_lowrank_mass(const Dims& g, const void* q, const void* k, const float* wq,
-                               const float* wk, float tau, uint16_t* qtok, uint16_t* ktok,
-                               float* lbuf, double* scores, hipStream_t s);
+                               const float* wk, double tau, double* qtok, double* ktok,
+                               double* lbuf, double* scores, hipStream_t s);
 hipError_t launch_lowrank_max(const Dims& g, const void* q, const void* k, const float* wq,
-                              const float* wk, uint16_t* qtok, uint16_t* ktok, double* scores,
+                              const float* wk, double* qtok, double* ktok, double* scores,
                               hipStream_t s);
 }  // namespace sa

@@ -119,11 +119,9 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
  *                     token-pair scores
  *   SA_SCORE_LOWRANK_MAX: S[h,i,j] = max over valid tokens a of block i and b
  *                     of block j of <q_a Wq[h], k_b Wk[h]> (rank 16; the
- *                     projections are fp64 sums rounded to fp32, each split
- *                     into bf16 hi + lo; a token-pair score is the fp32 sum of
- *                     the hi.hi, hi.lo and lo.hi products on the matrix cores,
- *                     within about 2^-16 sum_c |q~_c k~_c| of the exact one;
- *                     S is their max)
+ *                     projections are fp64 sums and the token-pair scores
+ *                     fp64 dot products on the matrix cores, so S is exact
+ *                     to fp64 rounding)
  *   SA_SCORE_LOWRANK_MASS: with the predicted token scores read as logits
  *                     z_ab = tau <q_a Wq[h], k_b Wk[h]> (tau = score_scale,
  *                     0 -> 1/sqrt(d); valid keys only), S[h,i,j] = ln of the
@@ -131,9 +129,12 @@ int sa_workspace_size(const sa_problem* prob, int stage, size_t* bytes);
  *                     mass sum_{b in j} exp(z_ab) / sum_b exp(z_ab).  Rows of
  *                     exp(S) sum to one, so SA_TOP_P's softmax gives back the
  *                     masses.  Rank 16; token scores as for
- *                     SA_SCORE_LOWRANK_MAX, fp32 exponentials and sums;
- *                     the workspace holds ln sum_{b in j} exp(z_ab) for every
- *                     query token and key block (4*H*nKB*q_rows bytes).
+ *                     SA_SCORE_LOWRANK_MAX; each exponential is 2^n exp2(f)
+ *                     with f in [-1, 0] formed in fp64 and exp2 in fp32, all
+ *                     sums and logarithms fp64 (S within about 2^-22 of the
+ *                     exact value); the workspace holds
+ *                     ln sum_{b in j} exp(z_ab) for every query token and key
+ *                     block in fp64 (8*H*nKB*q_rows bytes).
  *   SA_TOP_P: P = softmax_j S[h,i,:]; blocks ordered by P descending, ties to
  *             the lower j; keep the shortest prefix whose cumulative mass
  *             reaches top_p (all blocks if top_p >= 1 or the prefix never

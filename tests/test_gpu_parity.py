@@ -63,8 +63,6 @@ def check_selection(w, sa, x, rows_to_check=None):
     if nkb % 32:
         assert np.all(bits[:, -1] >> np.uint32(nkb % 32) == 0)
     excused = 0
-    rel = (tokenmax_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MAX else
-           tokenmass_rel(w, x, s) if w.score_mode == I.SCORE_LOWRANK_MASS else None)
     for h in range(w.heads):
         for i in range(w.n_qb):
             if w.select_mode == I.SELECT_TOP_P:
@@ -74,60 +72,11 @@ def check_selection(w, sa, x, rows_to_check=None):
             want = np.zeros(nkb, bool)
             want[rec.order[:rec.m]] = True
             if not np.array_equal(want, mask[h, i]):
-                r = 1e-6 if rel is None else max(1e-6, float(rel[h, i]))
                 assert O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, mask[h, i],
-                                              rel=r), \
+                                              rel=1e-6), \
                     f"selection mismatch at head {h} query block {i}"
                 excused += 1
     return mask, excused
-
-
-def tokenmax_rel(w, x, s):
-    """Near-tie tolerance of the token-level max scores, per row.  The GPU
-    rounds the projected tokens to fp32, splits each into bf16 hi + lo and
-    sums hi.hi + hi.lo + lo.hi in fp32: a 16-term dot product is within about
-    2^-16 sum_c |q~_c k~_c| <= 2^-16 |q~_a| |k~_b| of the exact one (doubled
-    for margin), so a block score is within delta = 2^-15 max_a |q~_a|
-    max_b |k~_b|.  Top-k compares scores (relative to the row's max |S|),
-    top-p softmax masses (relative error up to 2 delta)."""
-    qt = np.matmul(x["q"][:, :w.q_valid].astype(np.float64), x["wq"].astype(np.float64))
-    kt = np.matmul(x["k"][:, :w.kv_valid].astype(np.float64), x["wk"].astype(np.float64))
-    qn = np.linalg.norm(qt, axis=2)
-    kn = np.linalg.norm(kt, axis=2).max(axis=1)                          # [H]
-    rel = np.zeros((w.heads, w.n_qb))
-    for i in range(w.n_qb):
-        lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
-        delta = 2.0 ** -15 * qn[:, lo:hi].max(axis=1) * kn
-        if w.select_mode == I.SELECT_TOP_K:
-            rel[:, i] = delta / np.abs(s[:, i]).max(axis=1)
-        else:
-            rel[:, i] = 2 * delta
-    return rel
-
-
-def tokenmass_rel(w, x, s):
-    """Near-tie tolerance of the predicted-mass scores, per row.  A logit
-    tau * q~.k~ is within tau * delta of the exact one (delta as in
-    tokenmax_rel: split-bf16 products of the fp32 projections); the fp32
-    exponentials, logarithms and sums add at most about 64 * 2^-24 to the
-    log-masses.  So ln M (the score S) is within eps = 2 (tau delta + 2^-18)
-    of the exact one, i.e. M is within relative eps.  Top-k compares S
-    (relative to the row's max |S|), top-p the masses (relative, 2 eps for
-    margin)."""
-    qt = np.matmul(x["q"][:, :w.q_valid].astype(np.float64), x["wq"].astype(np.float64))
-    kt = np.matmul(x["k"][:, :w.kv_valid].astype(np.float64), x["wk"].astype(np.float64))
-    qn = np.linalg.norm(qt, axis=2)
-    kn = np.linalg.norm(kt, axis=2).max(axis=1)                          # [H]
-    tau = w.eff_score_scale
-    rel = np.zeros((w.heads, w.n_qb))
-    for i in range(w.n_qb):
-        lo, hi = i * w.block, min((i + 1) * w.block, w.q_valid)
-        eps = 2.0 * (tau * 2.0 ** -15 * qn[:, lo:hi].max(axis=1) * kn + 2.0 ** -18)
-        if w.select_mode == I.SELECT_TOP_K:
-            rel[:, i] = eps / np.abs(s[:, i]).max(axis=1)
-        else:
-            rel[:, i] = 2 * eps
-    return rel
 
 
 def check_csr_demand_pack(w, sa, mask, x):
