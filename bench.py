@@ -32,7 +32,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_480p_32k.md")
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc", "attn_fwd.hip")
+# the attention forward's source: the kernel file and the headers it includes
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc", f)
+                for f in ("attn_fwd.hip", "attend_bf16.h", "mfma_bf16.h", "sa_common.h")]
 
 
 def parse():
@@ -64,14 +66,18 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(config_name, nnz):
     """HBM bytes per attention launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, only if it was taken on the current kernel source and workload."""
+    summary, only if it was taken on the current kernel source (the digest of
+    ATTN_SOURCES) and workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             line = next((l for l in f if l.startswith("traffic-record:")), None)
@@ -79,7 +85,7 @@ def load_traffic(config_name, nnz):
     except (OSError, ValueError):
         return None
     r = rec.get(config_name)
-    if not r or r.get("source_sha256") != source_digest(ATTN_SOURCE) or r.get("nnz") != nnz:
+    if not r or r.get("source_sha256") != source_digest(ATTN_SOURCES) or r.get("nnz") != nnz:
         return None
     return r.get("bytes_per_launch")
 
