@@ -44,6 +44,16 @@ struct CsrBlockList {
     if ((unsigned)j >= (unsigned)nkb) return -1;
     return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(col_slot[e]) : (int64_t)h * nkb + j;
   }
+  // entry e's values, loaded now and resolved after a later wait
+  struct Raw {
+    int j, slot;
+  };
+  __device__ __forceinline__ Raw fetch(int e) const { return {col_idx[e], col_slot ? col_slot[e] : 0}; }
+  __device__ __forceinline__ int64_t src_of(const Raw& r, int& j) const {
+    j = __builtin_amdgcn_readfirstlane(r.j);
+    if ((unsigned)j >= (unsigned)nkb) return -1;
+    return col_slot ? (int64_t)__builtin_amdgcn_readfirstlane(r.slot) : (int64_t)h * nkb + j;
+  }
 };
 
 // Key block list held in LDS (16-bit block ids of head h, full K/V).
@@ -53,6 +63,14 @@ struct LdsBlockList {
   __device__ __forceinline__ int col(int e) const { return __builtin_amdgcn_readfirstlane(ids[e]); }
   __device__ __forceinline__ int64_t src(int e) const {
     const int j = col(e);
+    return (unsigned)j < (unsigned)nkb ? (int64_t)h * nkb + j : -1;
+  }
+  struct Raw {
+    int j, slot;
+  };
+  __device__ __forceinline__ Raw fetch(int e) const { return {ids[e], 0}; }
+  __device__ __forceinline__ int64_t src_of(const Raw& r, int& j) const {
+    j = __builtin_amdgcn_readfirstlane(r.j);
     return (unsigned)j < (unsigned)nkb ? (int64_t)h * nkb + j : -1;
   }
 };
@@ -113,21 +131,35 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     for (int r = 0; r < 16; ++r) st.oacc[u][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // The list entry after the current block is loaded one block ahead and
+  // resolved after that block's closing wait, so that no block starts by
+  // waiting on a global load.
   int e = e0;
   int64_t blk = -1;
   while (e < e1 && (blk = list.src(e)) < 0) ++e;
+  int j = e < e1 ? list.col(e) : 0;
+  typename List::Raw rn{0, 0};
   if (e < e1) {
     dma_block(k + blk * (kB * kD), kl, wave, kvo);
     dma_block(v + blk * (kB * kD), vl, wave, vvo);
+    if (e + 1 < e1) rn = list.fetch(e + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   while (e < e1) {
-    const int j = list.col(e);
-    int en = e + 1;
+    // the next block: entry e + 1 (already loaded), or a later one if it is skipped
+    int en = e + 1, jn = 0;
     int64_t bn = -1;
-    while (en < e1 && (bn = list.src(en)) < 0) ++en;
+    if (en < e1) {
+      bn = list.src_of(rn, jn);
+      if (bn < 0) {
+        ++en;
+        while (en < e1 && (bn = list.src(en)) < 0) ++en;
+        if (en < e1) jn = list.col(en);
+      }
+    }
+    if (en + 1 < e1) rn = list.fetch(en + 1);
 
     // S^T tile t: keys 32t.., this lane's query; reg r -> key 32t + 8(r/4) + 4g + r%4
     f32x16 sacc[4];
@@ -221,6 +253,7 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     __syncthreads();
     if (en < e1) dma_block(v + bn * (kB * kD), vl, wave, vvo);
     e = en;
+    j = jn;
   }
   st.m_run = m_run;
   st.l_run = l_run;
