@@ -167,14 +167,24 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+    // K fragments of step s + 1 are read while the MFMAs of step s run
+    bf16x8 kf[2][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int t = 0; t < 4; ++t)
+      kf[0][t] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kl) + ka[0] +
+                                                  t * 8192);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            reinterpret_cast<const char*>(kl) + ka[s] + t * 8192);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          kf[(s + 1) & 1][t] = *reinterpret_cast<const bf16x8*>(
+              reinterpret_cast<const char*>(kl) + ka[s + 1] + t * 8192);
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], qf[s], sacc[t], 0, 0, 0);
+    }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
     __syncthreads();
@@ -223,6 +233,18 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g (the transposing reads
     // at rows 4 kga + e and 4 (kga + 2) + e).  The exp of tile t+1 is
     // independent of the MFMAs of tile t, so the two can overlap.
+    // V^T fragments of k-step (t, h2): d-tile u, keys 32t + 16h2 .. +16
+    auto vfrag = [&](int t, int h2, u32x4 (&vw)[4]) {
+      const int rows = 1024 * (8 * t + 4 * h2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x2 lo = lds_read_tr(vl, va[u] + rows);
+        const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
+        vw[u] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+    u32x4 vw[2][4];   // the fragments of the next k-step are read during this one's MFMAs
+    vfrag(0, 0, vw[0]);
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -234,16 +256,13 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
+        const int ks = 2 * t + h2;
+        if (ks + 1 < 8) vfrag((ks + 1) >> 1, (ks + 1) & 1, vw[(ks + 1) & 1]);
         const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
-        const int rows = 1024 * (8 * t + 4 * h2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x2 lo = lds_read_tr(vl, va[u] + rows);
-          const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
-          const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
-          st.oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
-                                                               st.oacc[u], 0, 0, 0);
-        }
+        for (int u = 0; u < 4; ++u)
+          st.oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, vw[ks & 1][u]), pf, st.oacc[u], 0, 0, 0);
       }
     }
     l_run += ps;
