@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="480p",
-                    help="tiny | 480p | 720p_rank | lowrank | hetero | lowrank_max | lowrank_mass")
+                    help="tiny | 480p | 720p_rank | lowrank | hetero | hetero_scale1 | lowrank_max | lowrank_mass")
     ap.add_argument("--unpacked", action="store_true", help="attend straight from K/V (no pack)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,6 +374,8 @@ def main():
         rec["dense_context"] = dense_context(w, d, sa, flush, packed, flops)
         if w.select_mode == 1 and w.score_mode in (0, 1) and not tiles:
             rec["fused"] = fused_leg(w, d, sa, flush, args.steps, ms_step, flops)
+        if w.name == "hetero_40h_32k" and not tiles:
+            rec["hetero_scale1"] = scale1_leg(w, d, sa, flush, packed)
     if not args.no_cpu_baseline:
         parity, rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items, sa)
         rec["parity"] = parity
@@ -463,14 +465,16 @@ def load_balance(sa, packed, flush, reps=5):
     # alternating so that neither gains from running second
     pers, unit = [], []
     for r in range(reps):
-        pers.append(_timed(lambda: sa.forward(packed=packed), flush, 1))
+        pers.append(_timed(lambda: sa.forward(packed=packed,
+                                              schedule=binding.SA_SCHEDULE_PERSISTENT), flush, 1))
         unit.append(_timed(lambda: sa.forward(packed=packed,
                                               schedule=binding.SA_SCHEDULE_PER_UNIT), flush, 1))
     return {"workgroups": n, "busy_max_over_mean": round(float(np.median(imb)), 4),
             "span_over_mean_busy": round(float(np.median(span)), 4),
             "persistent_forward_ms": round(float(np.median(pers)), 4),
             "per_unit_workgroups": sa.workgroups(binding.SA_SCHEDULE_PER_UNIT),
-            "per_unit_forward_ms": round(float(np.median(unit)), 4), "reps": reps}
+            "per_unit_forward_ms": round(float(np.median(unit)), 4), "reps": reps,
+            "default_schedule": "per_unit" if sa.w.select_mode == binding.SA_TOP_K else "persistent"}
 
 
 def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
@@ -514,6 +518,36 @@ def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
             "three_call_ms_per_layer": round(three_call_ms, 4),
             "speedup_over_three_call": round(three_call_ms / ms, 3),
             "same_mask_as_three_call": same, "steps": steps}
+
+
+def scale1_leg(w, d, sa, flush, packed, reps=5):
+    """The 40-head inputs selected at temperature 1 (score_scale 1): heads
+    keep from about 2% to over 90% of their blocks, the per-head spread of
+    the Top-p abstract's stragglers.  Reports that spread and both work
+    schedules' forward (load_balance)."""
+    import numpy as np
+    from block_sparse_attention_scores_amd import inputs as I
+    from block_sparse_attention_scores_amd.path import SparseAttention
+    ws = I.named("hetero_scale1")
+    s1 = SparseAttention(ws, sa.q, sa.k, sa.v, d.get("wq"), d.get("wk"))
+    s1.select()
+    if packed:
+        s1.pack()
+    rp = s1.row_ptr.cpu().numpy().astype(np.int64)
+    per_head = (rp[ws.n_qb::ws.n_qb][:ws.heads] - rp[:-1:ws.n_qb][:ws.heads]) / (ws.n_qb * ws.n_kb)
+    nnz = s1.nnz()
+    flops = 4.0 * ws.block * ws.block * ws.head_dim * nnz
+    lb = load_balance(s1, packed, flush, reps)
+    out = {"workload": ws.name, "score_scale": ws.score_scale, "selected_blocks": int(nnz),
+           "selected_fraction": round(nnz / (ws.heads * ws.n_qb * ws.n_kb), 4),
+           "per_head_selected_fraction": {
+               "min": round(float(per_head.min()), 4), "p25": round(float(np.percentile(per_head, 25)), 4),
+               "median": round(float(np.median(per_head)), 4), "max": round(float(per_head.max()), 4)},
+           "load_balance": lb,
+           "persistent_tflops": round(flops / (lb["persistent_forward_ms"] / 1e3) / 1e12, 3),
+           "per_unit_tflops": round(flops / (lb["per_unit_forward_ms"] / 1e3) / 1e12, 3)}
+    del s1
+    return out
 
 
 def dense_context(w, d, sa, flush, packed, flops, reps=5):

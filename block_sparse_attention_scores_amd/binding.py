@@ -30,7 +30,7 @@ SA_TOP_P, SA_TOP_K = 0, 1
 SA_SCORE_POOLED, SA_SCORE_LOWRANK, SA_SCORE_LOWRANK_MAX, SA_SCORE_LOWRANK_MASS = 0, 1, 2, 3
 SA_STAGE_SELECT, SA_STAGE_CSR, SA_STAGE_PACK, SA_STAGE_FORWARD, SA_STAGE_BACKWARD = 0, 1, 2, 3, 4
 SA_STAGE_FUSED = 5
-SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT = 0, 1
+SA_SCHEDULE_PERSISTENT, SA_SCHEDULE_PER_UNIT, SA_SCHEDULE_AUTO = 0, 1, 2
 
 EXPORTS = ("sa_workspace_size", "sparse_attn_select", "sparse_attn_csr_from_mask",
            "kv_demand_pack", "sparse_attn_forward", "sa_forward_workgroups",

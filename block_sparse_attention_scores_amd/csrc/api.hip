@@ -197,7 +197,7 @@ int check_forward_args(const Dims& g, const void* q, const int32_t* row_ptr,
 
 extern "C" {
 
-int sa_abi_version(void) { return 6; }
+int sa_abi_version(void) { return 7; }
 
 const char* sa_status_string(int status) {
   switch (status) {
@@ -307,12 +307,20 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr, const int32_t
   return SA_OK;
 }
 
+// SA_SCHEDULE_AUTO resolved for this problem; -1 for an unknown schedule
+static int resolve_schedule(const sa_problem* prob, int32_t schedule) {
+  if (schedule == SA_SCHEDULE_AUTO)
+    return prob->select_mode == SA_TOP_K ? SA_SCHEDULE_PER_UNIT : SA_SCHEDULE_PERSISTENT;
+  return schedule == SA_SCHEDULE_PERSISTENT || schedule == SA_SCHEDULE_PER_UNIT ? schedule : -1;
+}
+
 int sa_forward_workgroups(const sa_problem* prob, int32_t schedule, int32_t* workgroups) {
   Dims g;
   const int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
   if (!workgroups) return SA_ERR_INVALID_ARG;
-  if (schedule != SA_SCHEDULE_PERSISTENT && schedule != SA_SCHEDULE_PER_UNIT) return SA_ERR_INVALID_ARG;
+  schedule = resolve_schedule(prob, schedule);
+  if (schedule < 0) return SA_ERR_INVALID_ARG;
   if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
   *workgroups = sa::attn_workgroups(g, schedule);
   return SA_OK;
@@ -327,12 +335,10 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q, const int32_t*
   if (st != SA_OK) return st;
   st = check_forward_args(g, q, row_ptr, col_idx, k_src, v_src, out, lse_opt);
   if (st != SA_OK) return st;
-  int schedule = SA_SCHEDULE_PERSISTENT;
+  int schedule = resolve_schedule(prob, opts ? opts->schedule : SA_SCHEDULE_AUTO);
   uint64_t* wg_clock = nullptr;
+  if (schedule < 0) return SA_ERR_INVALID_ARG;
   if (opts) {
-    schedule = opts->schedule;
-    if (schedule != SA_SCHEDULE_PERSISTENT && schedule != SA_SCHEDULE_PER_UNIT)
-      return SA_ERR_INVALID_ARG;
     if (opts->wg_clock && g.dtype == SA_BF16) {
       if (((uintptr_t)opts->wg_clock & 7u) || opts->clock_cap < sa::attn_workgroups(g, schedule))
         return SA_ERR_INVALID_ARG;
@@ -407,7 +413,7 @@ int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int
   if (!ws) return SA_ERR_HIP;
   const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
   SA_TRY_HIP(sa::launch_attn(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt, ws,
-                             need, sm, SA_SCHEDULE_PERSISTENT, nullptr,
+                             need, sm, resolve_schedule(prob, SA_SCHEDULE_AUTO), nullptr,
                              static_cast<hipStream_t>(stream)));
   return SA_OK;
 }

@@ -155,6 +155,14 @@ def hetero() -> Workload:
                     strength_range=(0.05, 2.0), top_p=0.95, top_k=4)
 
 
+def hetero_scale1() -> Workload:
+    """The 40-head workload with block scores at temperature 1 (score_scale 1
+    in place of 1/sqrt(d)): the sharper softmax spreads the heads from about
+    2% to over 90% of their blocks kept, the per-head spread of the Top-p
+    abstract's straggler setting (same inputs as hetero)."""
+    return dataclasses.replace(hetero(), name="hetero_40h_32k_scale1", score_scale=1.0)
+
+
 def lowrank_max() -> Workload:
     """The low-rank workload with token-level predicted scores aggregated by
     the max over each block pair (same inputs, same W, same top-k)."""
@@ -170,8 +178,8 @@ def lowrank_mass() -> Workload:
 
 
 NAMED = {"tiny": tiny, "480p": c480p, "720p_rank": c720p_rank,
-         "lowrank": lowrank, "hetero": hetero, "lowrank_max": lowrank_max,
-         "lowrank_mass": lowrank_mass}
+         "lowrank": lowrank, "hetero": hetero, "hetero_scale1": hetero_scale1,
+         "lowrank_max": lowrank_max, "lowrank_mass": lowrank_mass}
 
 
 def named(name: str) -> Workload:

@@ -196,8 +196,10 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr,
  * col_slot == NULL: k_src, v_src are the full K, V [H,kv_rows,d].
  * col_slot != NULL: k_src, v_src are packed [slots,B,d] and entry e reads
  *                   slot col_slot[e] (col_idx still gives the block id).
- * Work items (head, query block) are processed head by head, longest first
- * within a head.  When whole items would leave the device's last round of
+ * Work items (head, query block) are cut into eight contiguous ranges of
+ * near-equal work, one per XCD, and taken in (head, query block) order within
+ * a range, under the schedule SA_SCHEDULE_AUTO picks for the problem (see
+ * sa_schedule).  When whole items would leave the device's last round of
  * work more than 5% idle, each item's block list is processed as two halves
  * whose partial results are combined in a fixed order, so results never
  * depend on timing; the workspace then also holds the halves' partial
@@ -212,12 +214,17 @@ int sparse_attn_forward(const sa_problem* prob, const void* q,
 
 /* Work schedules of the attention forward (sparse_attn_forward_ex). */
 typedef enum sa_schedule {
-  SA_SCHEDULE_PERSISTENT = 0, /* what sparse_attn_forward runs: two workgroups
-                                 per CU take work units from per-XCD queues
-                                 until all are done                           */
-  SA_SCHEDULE_PER_UNIT = 1    /* one workgroup per work unit, handed out by the
-                                 hardware dispatcher (the plain launch, kept as
-                                 a measured alternative)                      */
+  SA_SCHEDULE_PERSISTENT = 0, /* two workgroups per CU take work units from
+                                 per-XCD queues until all are done            */
+  SA_SCHEDULE_PER_UNIT = 1,   /* one workgroup per work unit, handed out by the
+                                 hardware dispatcher (the plain launch)       */
+  SA_SCHEDULE_AUTO = 2        /* what sparse_attn_forward runs: PER_UNIT when
+                                 prob->select_mode is SA_TOP_K (every row keeps
+                                 the same number of blocks, so the dispatcher
+                                 balances them and the queue only adds its
+                                 pops), PERSISTENT otherwise (rows of unequal
+                                 length, where the queue removes the
+                                 stragglers of the Top-p abstract)             */
 } sa_schedule;
 
 /* Options of sparse_attn_forward_ex (host struct, read synchronously). */
@@ -239,7 +246,7 @@ int sa_forward_workgroups(const sa_problem* prob, int32_t schedule, int32_t* wor
  * clock stamps, the measurement behind the load-imbalance figure (max over
  * mean of the workgroups' busy time) that the Top-p sparse-attention
  * abstract reports for its rank-level stragglers.  Results are bit-identical
- * to sparse_attn_forward's under either schedule.  The fp32 path always runs
+ * to sparse_attn_forward's under every schedule.  The fp32 path always runs
  * one workgroup per item and writes no clock stamps.  SA_ERR_INVALID_ARG for
  * an unknown schedule, or a wg_clock with clock_cap below
  * sa_forward_workgroups.  opts == NULL is sparse_attn_forward. */
@@ -368,7 +375,8 @@ const char* sa_status_string(int status);
 /* ABI version of this header: 6 (1, plus the video block order entry points
  * in 2, plus sparse_attn_backward in 3, plus sparse_attn_forward_ex and
  * sa_forward_workgroups in 4, plus sparse_attn_forward_noalloc and
- * SA_ERR_SCRATCH in 5, plus sparse_attn_fused and SA_STAGE_FUSED in 6). */
+ * SA_ERR_SCRATCH in 5, plus sparse_attn_fused and SA_STAGE_FUSED in 6, plus
+ * SA_SCHEDULE_AUTO, the per-problem schedule sparse_attn_forward runs, in 7). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 6
+    assert lib.sa_abi_version() == 7
 
 
 def test_struct_layout_matches_c():
@@ -236,7 +236,15 @@ def test_forward_ex_validation(lib):
     assert lib.sa_forward_workgroups(ctypes.byref(p), B.SA_SCHEDULE_PER_UNIT, ctypes.byref(wg)) == 0
     per_unit = wg.value
     assert 0 < persist <= per_unit
-    assert lib.sa_forward_workgroups(ctypes.byref(p), 2, ctypes.byref(wg)) == B.SA_ERR_INVALID_ARG
+    # SA_SCHEDULE_AUTO: the queue for top-p problems, the plain launch for top-k
+    assert lib.sa_forward_workgroups(ctypes.byref(p), B.SA_SCHEDULE_AUTO, ctypes.byref(wg)) == 0
+    assert wg.value == (per_unit if p.select_mode == B.SA_TOP_K else persist)
+    pk = good_problem(select_mode=B.SA_TOP_K, top_k=3)
+    assert lib.sa_forward_workgroups(ctypes.byref(pk), B.SA_SCHEDULE_AUTO, ctypes.byref(wg)) == 0
+    auto_k = wg.value
+    assert lib.sa_forward_workgroups(ctypes.byref(pk), B.SA_SCHEDULE_PER_UNIT, ctypes.byref(wg)) == 0
+    assert auto_k == wg.value
+    assert lib.sa_forward_workgroups(ctypes.byref(p), 3, ctypes.byref(wg)) == B.SA_ERR_INVALID_ARG
     assert lib.sa_forward_workgroups(ctypes.byref(p), 0, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_forward_workgroups(None, 0, ctypes.byref(wg)) == B.SA_ERR_INVALID_ARG
 
@@ -246,7 +254,7 @@ def test_forward_ex_validation(lib):
     def call(opts, args=base):
         return f(*args, ctypes.byref(opts), None)
 
-    assert call(B.SaForwardOpts(2, 0, None)) == B.SA_ERR_INVALID_ARG          # unknown schedule
+    assert call(B.SaForwardOpts(3, 0, None)) == B.SA_ERR_INVALID_ARG          # unknown schedule
     assert call(B.SaForwardOpts(-1, 0, None)) == B.SA_ERR_INVALID_ARG
     assert call(B.SaForwardOpts(B.SA_SCHEDULE_PERSISTENT, persist - 1, FAKE)) == B.SA_ERR_INVALID_ARG
     assert call(B.SaForwardOpts(B.SA_SCHEDULE_PER_UNIT, per_unit - 1, FAKE)) == B.SA_ERR_INVALID_ARG

@@ -34,7 +34,7 @@ def sampled_items(w, row_ptr, n_random=4, seed=0):
     return [(r // w.n_qb, r % w.n_qb) for r in sorted(pick)]
 
 
-@pytest.mark.parametrize("name", ["480p", "720p_rank", "lowrank", "hetero"])
+@pytest.mark.parametrize("name", ["480p", "720p_rank", "lowrank", "hetero", "hetero_scale1"])
 def test_full_size_workload(name):
     w = I.named(name)
     say("workload", w.name, "heads", w.heads, "q", w.q_valid, "kv", w.kv_valid)
