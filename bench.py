@@ -345,6 +345,12 @@ def main():
                           "permute_out": round(float(pout.mean()), 4)} if tiles else {}),
                       "forward_p10_p90": [round(float(np.percentile(fwd, 10)), 4),
                                           round(float(np.percentile(fwd, 90)), 4)]},
+        # median, p10 and p90 of every stage over the timed steps
+        "stages_ms_dist": {name: {"median": round(float(np.median(a)), 4),
+                                  "p10": round(float(np.percentile(a, 10)), 4),
+                                  "p90": round(float(np.percentile(a, 90)), 4)}
+                           for name, a in (("select", sel), ("pack", pck), ("forward", fwd),
+                                           ("step", tot))},
         "selected_blocks": nnz, "dense_blocks": dense_pairs,
         "selected_fraction": round(nnz / dense_pairs, 4),
         "demanded_blocks": demand, "selected_tflop": round(flops / 1e12, 4),

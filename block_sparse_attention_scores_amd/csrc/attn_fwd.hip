@@ -2,13 +2,13 @@
 // Large-Scale Video DiT Training", section "The idea": sparse attention
 // kernels that never build the full score matrix; neighbouring queries, one
 // query block, share one selected key/value set) with the work balanced over
-// the device so uneven per-head sparsity does not leave CUs idle (same page,
-// "Once the work is uneven"; the Top-p sparse-attention abstract, mlsift
-// listing: rank-level stragglers).
+// the device so uneven per-head sparsity does not leave CUs idle (same page
+// and section, the paragraph on uneven work; the Top-p sparse-attention
+// abstract, mlsift listing: rank-level stragglers).
 //
 // queue_kernel : one workgroup orders the work units (items, or halves of
-//                their block lists) into per-XCD ranges by a counting sort on
-//                (range, head, half, count); see "work queue" below.
+//                their block lists) into per-XCD ranges, in (range, head
+//                group, half, item) order; see "work queue" below.
 // attn_f32     : fp32 path (one thread per query, 32-key LDS sub-tiles,
 //                online softmax in fp32), one workgroup per item.
 // attn_bf16    : bf16 MFMA path, d = 128, block = 128, persistent: each

@@ -372,10 +372,10 @@ QUEUE_MAX_GROUPS = 4096   # (range, head group, half) groups the device's sort c
 def work_order(row_ptr: np.ndarray, n_qb: int, split: bool, ranges: int = QUEUE_RANGES,
                max_groups: int = QUEUE_MAX_GROUPS):
     """Order of the attention's work units.  The pages ask only that uneven
-    per-head work be spread so that no worker straggles (DSV explainer, "Once
-    the work is uneven": reallocate heads by their sparse workload; Top-p
-    abstract: sparse attention becomes a rank-level straggler problem); the
-    order itself is this reading:
+    per-head work be spread so that no worker straggles (DSV explainer, "The
+    idea", the paragraph on uneven work: reallocate heads by their sparse
+    workload; Top-p abstract: sparse attention becomes a rank-level straggler
+    problem); the order itself is this reading:
 
     * An item is one (head, query block) row r (rows head-major).  With
       ``split`` every row of c >= 2 selected blocks is two units, its first
