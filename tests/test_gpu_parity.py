@@ -206,6 +206,9 @@ def test_lowrank_top_k():
                    select_mode=I.SELECT_TOP_K, top_k=3, score_mode=I.SCORE_LOWRANK, seed=25)
     sa, _, mask = full_check(w)
     assert np.all(mask.sum(axis=2) == 3)
+    # top-k: the default schedule is one workgroup per unit; all three agree
+    assert sa.workgroups(B.SA_SCHEDULE_AUTO) == sa.workgroups(B.SA_SCHEDULE_PER_UNIT)
+    check_schedules(sa)
 
 
 @pytest.mark.parametrize("mode,p,k", [(I.SELECT_TOP_K, 0.9, 5), (I.SELECT_TOP_P, 0.6, 2)])
@@ -387,10 +390,10 @@ def test_whole_items_when_rows_fill_the_grid():
 
 
 def check_schedules(sa):
-    """Both work schedules give the persistent result bit for bit; every
-    workgroup stamps a start and an end."""
+    """Every work schedule gives the default forward's result bit for bit;
+    every workgroup stamps a start and an end."""
     o1, l1 = sa.out.clone(), sa.lse.clone()
-    for sched in (B.SA_SCHEDULE_PER_UNIT, B.SA_SCHEDULE_PERSISTENT):
+    for sched in (B.SA_SCHEDULE_PER_UNIT, B.SA_SCHEDULE_PERSISTENT, B.SA_SCHEDULE_AUTO):
         n = sa.workgroups(sched)
         clk = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
         sa.out.zero_()
