@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,8 +41,8 @@ ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_scores_amd", "csrc", 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="480p",
                     help="tiny | 480p | 720p_rank | lowrank | hetero | hetero_scale1 | lowrank_max | lowrank_mass")
     ap.add_argument("--unpacked", action="store_true", help="attend straight from K/V (no pack)")
@@ -152,7 +153,20 @@ def cpu_baseline(w, x, n_items, sa=None):
                        f"masked attention for the sample ({t_att:.2f} s) + fp64 selection, CSR, "
                        f"demand and pack of " + ("the sampled rows" if token else "all rows") +
                        f" ({t_sel:.2f} s) pro-rated by {n_items}/{sel_rows}"),
-            "seconds": round(t_att + t_sel, 3), "host_cpus": os.cpu_count()}
+            "seconds": round(t_att + t_sel, 3), "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def parity_report(w, x, sa, mask_ref, recs, items, o_ref, lse_ref):
@@ -382,6 +396,7 @@ def main():
             rec["fused"] = fused_leg(w, d, sa, flush, args.steps, ms_step, flops)
         if w.name == "hetero_40h_32k" and not tiles:
             rec["hetero_scale1"] = scale1_leg(w, d, sa, flush, packed)
+        rec["machine"] = machine_context(flush)
     if not args.no_cpu_baseline:
         parity, rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_items, sa)
         rec["parity"] = parity
@@ -408,6 +423,47 @@ def _timed(fn, flush, reps):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     return float(np.median(ts))
+
+
+def machine_context(flush, reps=5):
+    """Context for the roofline fractions, measured on this GPU: compute-unit
+    count and architecture (device properties), the engine clock rocminfo
+    lists, a 1 GiB device copy (flushed, median of `reps`; read + write bytes
+    over time) and a dense bf16 GEMM through torch.mm (the vendor BLAS,
+    8192 x 8192 x 8192, median of `reps` after one untimed call)."""
+    import subprocess
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    ctx = {"cu_count": props.multi_processor_count, "arch": props.gcnArchName.split(":")[0]}
+    try:
+        r = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60)
+        clock = None
+        for agent in re.split(r"\n\*+\s*\n\s*Agent \d+", r.stdout)[1:]:
+            name = re.search(r"^\s*Name:\s*(\S+)", agent, re.M)
+            mhz = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", agent)
+            if name and mhz and name.group(1).startswith("gfx"):
+                clock = int(mhz.group(1))
+                break
+        ctx["rocminfo_max_clock_mhz"] = clock
+    except (OSError, subprocess.SubprocessError):
+        ctx["rocminfo_max_clock_mhz"] = None
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _timed(lambda: dst.copy_(src), flush, reps)
+    ctx["copy_1gib_gbs"] = round(2 * n / (ms / 1e3) / 1e9, 1)
+    del src, dst
+    m = 8192
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn(m, m, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    ms = _timed(lambda: torch.mm(a, b, out=c), flush, reps)
+    ctx["gemm_bf16_8192_tflops"] = round(2.0 * m ** 3 / (ms / 1e3) / 1e12, 1)
+    del a, b, c
+    torch.cuda.synchronize()
+    return ctx
 
 
 def graph_step(sa, packed, flush, steps, eager_ms):
