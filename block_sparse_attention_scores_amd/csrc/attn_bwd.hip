@@ -155,14 +155,14 @@ __device__ __forceinline__ bf16x8 cols_a(const uint16_t* tile, const Offsets& o,
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// fragments of row `row` of a [rows, 128] bf16 tensor as the B operand:
-// k-step s holds columns 16s + 8g .. +8
-__device__ __forceinline__ void load_b(bf16x8 (&f)[8], const uint16_t* base, int64_t row,
-                                       int64_t rows, int g) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)(rows * kD * 2));
+// fragments of row `row` (0..127) of one 128-row block of a [rows, 128] bf16
+// tensor as the B operand: k-step s holds columns 16s + 8g .. +8 (the
+// descriptor spans the block only, so its offsets stay small at any length)
+__device__ __forceinline__ void load_b(bf16x8 (&f)[8], const uint16_t* block, int row, int g) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(block, kTileBytes);
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    f[s] = __builtin_bit_cast(bf16x8, buf_load16(r, (int)(row * 256) + 16 * g, 32 * s));
+    f[s] = __builtin_bit_cast(bf16x8, buf_load16(r, row * 256 + 16 * g, 32 * s));
 }
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int64_t qbase = (int64_t)h * q_rows;
 
   bf16x8 qf[8], df[8];
-  load_b(qf, q + qbase * kD, qrow, q_rows, g);
-  load_b(df, dout + qbase * kD, qrow, q_rows, g);
+  load_b(qf, q + (qbase + (int64_t)i * kB) * kD, 32 * wave + lq, g);
+  load_b(df, dout + (qbase + (int64_t)i * kB) * kD, 32 * wave + lq, g);
   const float l = lse[qbase + qrow];
   const bool live = qrow < q_valid && l > -INFINITY;
   const float lse2 = live ? l * kLog2e : INFINITY;   // +inf: P = 0
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const bool key_ok = krow < kv_valid;
 
   bf16x8 kf[8], vf[8];
-  load_b(kf, k + kbase * kD, krow, kv_rows, g);
-  load_b(vf, v + kbase * kD, krow, kv_rows, g);
+  load_b(kf, k + (kbase + (int64_t)j * kB) * kD, 32 * wave + lq, g);
+  load_b(vf, v + (kbase + (int64_t)j * kB) * kD, 32 * wave + lq, g);
 
   f32x16 dka[4], dva[4];
 #pragma unroll
