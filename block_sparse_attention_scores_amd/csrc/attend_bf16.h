@@ -167,7 +167,9 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-    // K fragments of step s + 1 are read while the MFMAs of step s run
+    // K fragments of step s + 1 are read while the MFMAs of step s run.  The
+    // scheduling fences keep them there: left alone, the compiler folds the
+    // two fragment sets into one and waits on each read right before its MFMA.
     bf16x8 kf[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -181,9 +183,11 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
           kf[(s + 1) & 1][t] = *reinterpret_cast<const bf16x8*>(
               reinterpret_cast<const char*>(kl) + ka[s + 1] + t * 8192);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][t], qf[s], sacc[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's V loads
@@ -231,40 +235,50 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     // per key tile t: P = exp2(S*scale - m), then O^T += V^T P^T over k-steps
     // (t, h2) covering keys 32t + 16h2 .. +16: slots 0-3 are keys 4*kga .. +3 and
     // slots 4-7 keys 4*(kga+2) .. +3, kga = 8t + 4h2 + g (the transposing reads
-    // at rows 4 kga + e and 4 (kga + 2) + e).  The exp of tile t+1 is
-    // independent of the MFMAs of tile t, so the two can overlap.
-    // V^T fragments of k-step (t, h2): d-tile u, keys 32t + 16h2 .. +16
-    auto vfrag = [&](int t, int h2, u32x4 (&vw)[4]) {
-      const int rows = 1024 * (8 * t + 4 * h2);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x2 lo = lds_read_tr(vl, va[u] + rows);
-        const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
-        vw[u] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
+    // at rows 4 kga + e and 4 (kga + 2) + e).
+    // The 32 P V MFMAs run as one sequence (n: k-step n / 4 = 2t + h2, d-tile
+    // n % 4, so consecutive MFMAs feed different accumulators), each V
+    // fragment read kAhead MFMAs ahead into a ring of registers, and the
+    // exponentials of tile t + 1 spread over the MFMAs of tile t (two per
+    // MFMA); scheduling fences keep every MFMA in its place.  The row sum and
+    // every accumulator see their terms in the plain loop's order.
+    constexpr int kAhead = 4, kRing = 6;
+    auto vread = [&](auto nc) -> u32x4 {
+      constexpr int n = decltype(nc)::value, ks = n / 4, u = n % 4;
+      const int rows = 1024 * (8 * (ks >> 1) + 4 * (ks & 1));
+      const u32x2 lo = lds_read_tr(vl, va[u] + rows);
+      const u32x2 hi = lds_read_tr(vl, va[u] + rows + 2048);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    u32x4 vw[2][4];   // the fragments of the next k-step are read during this one's MFMAs
-    vfrag(0, 0, vw[0]);
+    u32x4 ring[kRing];
     float ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -mn));
-        sacc[t][r] = p;
-        ps += p;
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int ks = 2 * t + h2;
-        if (ks + 1 < 8) vfrag((ks + 1) >> 1, (ks + 1) & 1, vw[(ks + 1) & 1]);
-        const bf16x8 pf = to_bf16x8(sacc[t], 8 * h2);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          st.oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, vw[ks & 1][u]), pf, st.oacc[u], 0, 0, 0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[0][r], scale_log2, -mn));
+      sacc[0][r] = p;
+      ps += p;
     }
+    static_for<0, kAhead>([&](auto nc) { ring[decltype(nc)::value % kRing] = vread(nc); });
+    bf16x8 pf;
+    static_for<0, 32>([&](auto nc) {
+      constexpr int n = decltype(nc)::value, ks = n / 4, t = ks / 2, h2 = ks % 2, u = n % 4;
+      if constexpr (n + kAhead < 32)
+        ring[(n + kAhead) % kRing] = vread(std::integral_constant<int, n + kAhead>{});
+      if constexpr (t + 1 < 4) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int r = 2 * (n % 8) + x;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t + 1][r], scale_log2, -mn));
+          sacc[t + 1][r] = p;
+          ps += p;
+        }
+      }
+      if constexpr (u == 0) pf = to_bf16x8(sacc[t], 8 * h2);
+      __builtin_amdgcn_sched_barrier(0);
+      st.oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, ring[n % kRing]), pf, st.oacc[u], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     l_run += ps;
     __builtin_amdgcn_s_setprio(0);
 

@@ -15,7 +15,12 @@
 //                   the next V phase
 //   bwd_dkdv_kernel one workgroup per (head, key block): over its CSC column,
 //                   S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS;
-//                   two LDS buffers, the next query block loads during compute
+//                   two LDS buffers, the next query block loads during compute;
+//                   one wave per SIMD, so each wave runs its own software
+//                   pipeline: the exponentials of tile t between the score
+//                   MFMAs of tile t + 1
+// In both, operand fragments are read from LDS a few MFMAs ahead of their use
+// and scheduling fences hold the reads there.
 // All GEMMs are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are
 // rounded to bf16 as MFMA operands.  Blocks arrive in LDS through direct loads
 // with the K swizzle (logical 16-byte chunk c of row r at c ^ (r & 15)); the
@@ -24,6 +29,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mfma_bf16.h"
 
@@ -224,13 +230,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     while (en < e1 && (sn = src_of(en)) < 0) ++en;
     f32x16 dpacc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpacc[t][r] = 0.f;
+    // V rows read two fragments ahead of their MFMA; the scheduling fences
+    // keep them there (left alone, the compiler waits on each read right
+    // before its MFMA)
+    {
+      bf16x8 fv[32];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        dpacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(vl, off, t, s), df[s], dpacc[t],
-                                                           0, 0, 0);
+      for (int i = 0; i < 2; ++i) fv[i] = rows_a(vl, off, i >> 3, i & 7);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + 2 < 32) fv[i + 2] = rows_a(vl, off, (i + 2) >> 3, (i + 2) & 7);
+        __builtin_amdgcn_sched_barrier(0);
+        dpacc[i >> 3] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[i], df[i & 7], dpacc[i >> 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's K_j loads
     __syncthreads();
@@ -239,14 +256,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     // raised wave priority over the phase that mixes exponentials and MFMAs
     // (the other workgroup's wave on the SIMD fills in from its dP MFMAs)
     __builtin_amdgcn_s_setprio(1);
+    // K rows (fk, k-step i) and transposed K (fc, half j / 4, d-tile j % 4) read
+    // two fragments ahead of their MFMA, fenced
+    bf16x8 fk[8], fc[8];
+    fk[0] = rows_a(kl, off, 0, 0);
+    fk[1] = rows_a(kl, off, 0, 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(kl, off, t, s), qf[s], sacc, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        if (i + 2 < 8) fk[i + 2] = rows_a(kl, off, t, i + 2);
+        else fc[i - 6] = cols_a(kl, off, (i - 6) & 3, t, (i - 6) >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[i], qf[i], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // reg r: key 32t + 8(r/4) + 4g + r%4 of this lane's query
       f32x16 ds;
 #pragma unroll
@@ -255,13 +282,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         const float p = key < lim ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
         ds[r] = p * (dpacc[t][r] - dlt);
       }
+      const bf16x8 dsf[2] = {to_bf16x8(ds, 0), to_bf16x8(ds, 8)};
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 dsf = to_bf16x8(ds, 8 * h2);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(kl, off, u, t, h2), dsf, acc[u],
-                                                           0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        if (j + 2 < 8) fc[j + 2] = cols_a(kl, off, (j + 2) & 3, t, (j + 2) >> 2);
+        else if (t + 1 < 4) fk[j - 6] = rows_a(kl, off, t + 1, j - 6);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[j], dsf[j >> 2], acc[j & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -282,6 +310,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int x = 0; x < 4; ++x) o4[x] = acc[u][4 * r4 + x] * sc;
       *reinterpret_cast<bf16x4*>(op + 32 * u + 8 * r4 + 4 * g) = __builtin_convertvector(o4, bf16x4);
     }
+}
+
+// Element n of one query block's MFMA sequence in the dK/dV kernel: kind 0 =
+// A (score / dP, fragment idx of tile t), 1 = C (dV / dK, fragment idx of tile t).
+struct SeqElem {
+  int kind, t, idx;
+};
+__host__ __device__ constexpr SeqElem seq_elem(int n) {
+  if (n < 16) return {0, 0, n};
+  const int m = n - 16;
+  if (m >= 96) return {1, 3, m - 96};
+  const int b = m / 32, pos = m % 32;
+  return pos < 16 ? SeqElem{0, b + 1, pos} : SeqElem{1, b, pos - 16};
 }
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
@@ -342,45 +383,83 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* dl = dbuf[b];
     const float* lse_s = lse_b[b];
     const float* dlt_s = dlt_b[b];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x16 sacc, dpacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dpacc[r] = 0.f; }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(ql, off, t, s), kf[s], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rows_a(dl, off, t, s), vf[s], dpacc, 0, 0, 0);
-      }
-      // reg r: query 32t + 8(r/4) + 4g + r%4 against this lane's key
-      f32x16 p, ds;
+    // One wave per SIMD, so the wave must overlap its own work.  The MFMAs of
+    // one query block run as one sequence: A(0), then per tile t the score
+    // and dP MFMAs of tile t + 1 (A) with the exponentials of tile t between
+    // them, then tile t's dV/dK MFMAs (C).  Each operand fragment is read
+    // kAhead MFMAs before its use, into a ring of registers, and scheduling
+    // fences keep every MFMA in its place.  Per tile t:
+    //   A fragment i: rows of Q (i even) or dO (i odd), k-step i / 2;
+    //   C fragment j: transposed dO (j even) or Q (j odd), half j / 8, d-tile (j / 2) % 4.
+    // Every accumulator sees its terms in the plain loop's order.
+    constexpr int kAhead = 6, kRing = 8, kSeq = 128;
+    auto read = [&](auto nc) -> bf16x8 {
+      constexpr SeqElem e = seq_elem(decltype(nc)::value);
+      if constexpr (e.kind == 0) return rows_a((e.idx & 1) ? dl : ql, off, e.t, e.idx >> 1);
+      else return cols_a((e.idx & 1) ? ql : dl, off, (e.idx >> 1) & 3, e.t, e.idx >> 3);
+    };
+    bf16x8 ring[kRing];
+    f32x16 sacc[2], dpacc[2], p, ds;
+    f32x4 l4[4], d4[4];
+    bf16x8 pf[2], dsf[2];
+    // P and dS of tile t, entry r (query 32t + 8(r/4) + 4g + r%4, this lane's key)
+    auto softmax_r = [&](int t, int r) {
+      const float pv = key_ok ? __builtin_amdgcn_exp2f(fmaf(sacc[t & 1][r], scale_log2,
+                                                            -l4[r >> 2][r & 3]))
+                              : 0.f;
+      p[r] = pv;
+      ds[r] = pv * (dpacc[t & 1][r] - d4[r >> 2][r & 3]);
+    };
+    auto load_stats = [&](int t) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int q0 = 32 * t + 8 * r4 + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + q0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_s + q0);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * r4 + x;
-          const float pv =
-              key_ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l4[x])) : 0.f;
-          p[r] = pv;
-          ds[r] = pv * (dpacc[r] - d4[x]);
-        }
+        l4[r4] = *reinterpret_cast<const f32x4*>(lse_s + q0);
+        d4[r4] = *reinterpret_cast<const f32x4*>(dlt_s + q0);
       }
+    };
+    static_for<0, kAhead>([&](auto nc) { ring[decltype(nc)::value % kRing] = read(nc); });
+    static_for<0, kSeq>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      constexpr SeqElem e = seq_elem(n);
+      if constexpr (n + kAhead < kSeq)
+        ring[(n + kAhead) % kRing] = read(std::integral_constant<int, n + kAhead>{});
+      if constexpr (e.kind == 0) {
+        if constexpr (e.idx == 0) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 pf = to_bf16x8(p, 8 * h2);
-        const bf16x8 dsf = to_bf16x8(ds, 8 * h2);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(dl, off, u, t, h2), pf, dva[u],
-                                                           0, 0, 0);
-          dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cols_a(ql, off, u, t, h2), dsf, dka[u],
-                                                           0, 0, 0);
+          for (int r = 0; r < 16; ++r) { sacc[e.t & 1][r] = 0.f; dpacc[e.t & 1][r] = 0.f; }
         }
+        if constexpr (e.t >= 1) softmax_r(e.t - 1, e.idx);   // tile t - 1's statistics are loaded
+      } else if constexpr (e.idx == 0) {
+        if constexpr (e.t == 3) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) softmax_r(3, r);
+        }
+        pf[0] = to_bf16x8(p, 0);
+        pf[1] = to_bf16x8(p, 8);
+        dsf[0] = to_bf16x8(ds, 0);
+        dsf[1] = to_bf16x8(ds, 8);
+        if constexpr (e.t < 3) load_stats(e.t + 1);   // tile t is packed: its stats are free
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 f = ring[n % kRing];
+      if constexpr (e.kind == 0) {
+        if constexpr (e.idx & 1)
+          dpacc[e.t & 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vf[e.idx >> 1], dpacc[e.t & 1], 0, 0, 0);
+        else
+          sacc[e.t & 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kf[e.idx >> 1], sacc[e.t & 1], 0, 0, 0);
+      } else {
+        constexpr int u = (e.idx >> 1) & 3, h2 = e.idx >> 3;
+        if constexpr (e.idx & 1)
+          dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, dsf[h2], dka[u], 0, 0, 0);
+        else
+          dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[h2], dva[u], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (n == 0) load_stats(0);
+    });
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next block
     __syncthreads();
   }

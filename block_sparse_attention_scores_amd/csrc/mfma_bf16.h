@@ -3,6 +3,8 @@
 // direct HBM -> LDS block loads into XOR-swizzled rows, transposing LDS reads.
 #pragma once
 
+#include <type_traits>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -61,6 +63,15 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* base, int addr) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)(lds_void*)base + addr));
   return __builtin_bit_cast(u32x2, v);
+}
+
+// f(integral_constant<int, n>) for n = N .. End - 1, expanded at compile time
+template <int N, int End, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N < End) {
+    f(std::integral_constant<int, N>{});
+    static_for<N + 1, End>(f);
+  }
 }
 
 }  // namespace bf16mma
