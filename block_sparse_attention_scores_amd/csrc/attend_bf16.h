@@ -209,7 +209,14 @@ __device__ __forceinline__ void attend_blocks(AttnState& st, const List& list, i
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    {
+      // the two 32-lane halves hold the two key halves of each query: swapping
+      // them across registers (v_permlane32_swap) leaves each lane one copy
+      // of its own half's max and one of the other's
+      const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+      mx = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1])) * scale_log2;
+    }
     // The running max only moves when some query's block max exceeds it by
     // more than 8 (log2 units): until then P = exp2(S*scale - m) stays below
     // 2^8, and softmax does not depend on which reference max is used.  Most
