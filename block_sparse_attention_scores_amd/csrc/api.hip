@@ -113,7 +113,7 @@ PackWs pack_ws(const Dims& g) {
 }
 size_t forward_ws(const Dims& g) { return round_up(sa::attn_ws_bytes(g)); }
 struct BackwardWs {
-  size_t delta, bits, counts, col_ptr, row_idx, total;
+  size_t delta, bits, counts, col_ptr, row_idx, order, total;
 };
 BackwardWs backward_ws(const Dims& g) {
   BackwardWs w{};
@@ -123,6 +123,7 @@ BackwardWs backward_ws(const Dims& g) {
   w.counts = o; o += round_up(sizeof(int32_t) * g.H * g.nkb);
   w.col_ptr = o; o += round_up(sizeof(int32_t) * (g.H * g.nkb + 1));
   w.row_idx = o; o += round_up(sizeof(int32_t) * (size_t)g.H * g.nqb * g.nkb);
+  w.order = o; o += round_up(sizeof(int32_t) * g.H * g.nkb);
   w.total = o;
   return w;
 }
@@ -438,7 +439,8 @@ int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, c
   SA_TRY_HIP(sa::launch_backward(g, q, k, v, out, dout, lse, row_ptr, col_idx, dq, dk, dv,
                                  at<float>(ws, w.delta), at<uint32_t>(ws, w.bits),
                                  at<int32_t>(ws, w.counts),
-                                 at<int32_t>(ws, w.col_ptr), at<int32_t>(ws, w.row_idx), sm,
+                                 at<int32_t>(ws, w.col_ptr), at<int32_t>(ws, w.row_idx),
+                                 at<int32_t>(ws, w.order), sm,
                                  static_cast<hipStream_t>(stream)));
   return SA_OK;
 }

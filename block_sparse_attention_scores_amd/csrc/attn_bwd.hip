@@ -9,11 +9,12 @@
 //   row_bits_kernel the block mask rebuilt from the CSR (one wave per row)
 //   csc_*_kernel    the transpose of the block lists (per key block, the query
 //                   blocks that selected it, ascending): count, scan, fill
+//   lpt_order_kernel the dK/dV launch order: head by head, longest lists first
 //   bwd_dq_kernel   one workgroup per (head, query block): over its CSR row,
 //                   dP^T = V dO^T, then S^T = K Q^T, dS^T, dQ^T += K^T dS^T;
 //                   the next V loads during the K phase and the next K during
 //                   the next V phase
-//   bwd_dkdv_kernel one workgroup per (head, key block): over its CSC column,
+//   bwd_dkdv_kernel one workgroup per (head, key block), in that order: over its CSC column,
 //                   S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS;
 //                   two LDS buffers, the next query block loads during compute;
 //                   one wave per SIMD, so each wave runs its own software
@@ -118,6 +119,45 @@ __global__ __launch_bounds__(kScanThreads) void csc_scan_kernel(const int32_t* _
     __syncthreads();
   }
   if (threadIdx.x == 0) col_ptr[n] = base;
+}
+
+// Launch order of the dK/dV workgroups: head by head, and within a head the
+// key blocks by descending column length (longest first, so that the long
+// columns do not finish last, while the workgroups in flight still share one
+// head's Q and dO in the caches).  One workgroup per head counts lengths
+// 0..nqb into LDS bins; units of equal length land in the order their atomic
+// increments happen, which changes nothing but the schedule: every unit
+// writes only its own dK and dV.  Without room for the bins, the natural order.
+constexpr int kOrderThreads = 1024, kOrderBins = 4096;
+__global__ __launch_bounds__(kOrderThreads) void lpt_order_kernel(const int32_t* __restrict__ counts,
+                                                                   int nkb, int nqb,
+                                                                   int32_t* __restrict__ order) {
+  __shared__ int bins[kOrderBins];
+  __shared__ int scratch[kOrderThreads / kWave + 1];
+  const int t = threadIdx.x, nb = nqb + 1;
+  const int64_t u0 = (int64_t)blockIdx.x * nkb;   // this head's first unit
+  if (nb > kOrderBins) {
+    for (int j = t; j < nkb; j += kOrderThreads) order[u0 + j] = (int32_t)(u0 + j);
+    return;
+  }
+  for (int b = t; b < nb; b += kOrderThreads) bins[b] = 0;
+  __syncthreads();
+  for (int j = t; j < nkb; j += kOrderThreads) atomicAdd(&bins[nb - 1 - counts[u0 + j]], 1);
+  __syncthreads();
+  // exclusive scan of the bins (index nb - 1 - length: longest first), in chunks
+  int base = 0;
+  for (int b0 = 0; b0 < nb; b0 += kOrderThreads) {
+    const int b = b0 + t;
+    const int c = b < nb ? bins[b] : 0;
+    int total;
+    const int incl = block_inclusive_scan(c, scratch, &total);
+    __syncthreads();
+    if (b < nb) bins[b] = base + incl - c;
+    base += total;
+    __syncthreads();
+  }
+  for (int j = t; j < nkb; j += kOrderThreads)
+    order[u0 + atomicAdd(&bins[nb - 1 - counts[u0 + j]], 1)] = (int32_t)(u0 + j);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,14 +370,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int nqb, int nkb, int64_t q_rows,
-    int64_t q_valid, int64_t kv_rows, int64_t kv_valid, float scale_log2, float sm_scale) {
+    const int32_t* __restrict__ order, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int nqb, int nkb, int64_t q_rows, int64_t q_valid, int64_t kv_rows, int64_t kv_valid,
+    float scale_log2, float sm_scale) {
   // two buffers: the next query block loads while this one is computed
   __shared__ __attribute__((aligned(1024))) uint16_t qbuf[2][kB * kD];
   __shared__ __attribute__((aligned(1024))) uint16_t dbuf[2][kB * kD];
   __shared__ __attribute__((aligned(16))) float lse_b[2][kB];
   __shared__ __attribute__((aligned(16))) float dlt_b[2][kB];
-  const int unit = blockIdx.x;
+  const int unit = __builtin_amdgcn_readfirstlane(order[blockIdx.x]);
   const int h = unit / nkb, j = unit % nkb;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -386,7 +427,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // One wave per SIMD, so the wave must overlap its own work.  The MFMAs of
     // one query block run as one sequence: A(0), then per tile t the score
     // and dP MFMAs of tile t + 1 (A) with the exponentials of tile t between
-    // them, then tile t's dV/dK MFMAs (C).  Each operand fragment is read
+    // them, then tile t's dV/dK MFMAs (C); tile 3's exponentials sit between
+    // the C MFMAs of tile 2.  Each operand fragment is read
     // kAhead MFMAs before its use, into a ring of registers, and scheduling
     // fences keep every MFMA in its place.  Per tile t:
     //   A fragment i: rows of Q (i even) or dO (i odd), k-step i / 2;
@@ -400,22 +442,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     };
     bf16x8 ring[kRing];
     f32x16 sacc[2], dpacc[2], p, ds;
-    f32x4 l4[4], d4[4];
+    f32x4 l4[2][4], d4[2][4];   // LSE and D of tiles t and t + 1 (slot t & 1)
     bf16x8 pf[2], dsf[2];
     // P and dS of tile t, entry r (query 32t + 8(r/4) + 4g + r%4, this lane's key)
     auto softmax_r = [&](int t, int r) {
       const float pv = key_ok ? __builtin_amdgcn_exp2f(fmaf(sacc[t & 1][r], scale_log2,
-                                                            -l4[r >> 2][r & 3]))
+                                                            -l4[t & 1][r >> 2][r & 3]))
                               : 0.f;
       p[r] = pv;
-      ds[r] = pv * (dpacc[t & 1][r] - d4[r >> 2][r & 3]);
+      ds[r] = pv * (dpacc[t & 1][r] - d4[t & 1][r >> 2][r & 3]);
     };
     auto load_stats = [&](int t) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int q0 = 32 * t + 8 * r4 + 4 * g;
-        l4[r4] = *reinterpret_cast<const f32x4*>(lse_s + q0);
-        d4[r4] = *reinterpret_cast<const f32x4*>(dlt_s + q0);
+        l4[t & 1][r4] = *reinterpret_cast<const f32x4*>(lse_s + q0);
+        d4[t & 1][r4] = *reinterpret_cast<const f32x4*>(dlt_s + q0);
       }
     };
     static_for<0, kAhead>([&](auto nc) { ring[decltype(nc)::value % kRing] = read(nc); });
@@ -429,17 +471,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) { sacc[e.t & 1][r] = 0.f; dpacc[e.t & 1][r] = 0.f; }
         }
-        if constexpr (e.t >= 1) softmax_r(e.t - 1, e.idx);   // tile t - 1's statistics are loaded
-      } else if constexpr (e.idx == 0) {
-        if constexpr (e.t == 3) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) softmax_r(3, r);
+        if constexpr (e.t >= 1) softmax_r(e.t - 1, e.idx);
+      } else {
+        if constexpr (e.idx == 0) {
+          pf[0] = to_bf16x8(p, 0);
+          pf[1] = to_bf16x8(p, 8);
+          dsf[0] = to_bf16x8(ds, 0);
+          dsf[1] = to_bf16x8(ds, 8);
         }
-        pf[0] = to_bf16x8(p, 0);
-        pf[1] = to_bf16x8(p, 8);
-        dsf[0] = to_bf16x8(ds, 0);
-        dsf[1] = to_bf16x8(ds, 8);
-        if constexpr (e.t < 3) load_stats(e.t + 1);   // tile t is packed: its stats are free
+        // tile 3 has no score MFMAs after it: its P and dS are formed between
+        // the dV/dK MFMAs of tile 2 (p and ds are free once tile 2 is packed)
+        if constexpr (e.t == 2) softmax_r(3, e.idx);
       }
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 f = ring[n % kRing];
@@ -458,7 +500,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[h2], dva[u], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (n == 0) load_stats(0);
+      // the LSE and D of tile t are loaded as its score MFMAs start: they are
+      // used a tile later
+      if constexpr (e.kind == 0 && e.idx == 0) load_stats(e.t);
     });
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next block
     __syncthreads();
@@ -488,7 +532,8 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                            const void* out, const void* dout, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
                            void* dv, float* delta, uint32_t* bits, int32_t* counts,
-                           int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s) {
+                           int32_t* col_ptr, int32_t* row_idx, int32_t* order, float sm_scale,
+                           hipStream_t s) {
   const int64_t qrows_total = (int64_t)g.H * g.q_rows;
   hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((qrows_total + 3) / 4)), dim3(256), 0, s,
                      (const uint16_t*)out, (const uint16_t*)dout, qrows_total, g.q_rows,
@@ -503,6 +548,8 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, cols, col_ptr);
   hipLaunchKernelGGL(csc_kernel<true>, dim3(grid), dim3(256), 0, s, bits, g.H, g.nqb, g.nkb,
                      g.W, col_ptr, (int32_t*)nullptr, row_idx);
+  hipLaunchKernelGGL(lpt_order_kernel, dim3(g.H), dim3(kOrderThreads), 0, s, counts, g.nkb,
+                     g.nqb, order);
   const float scale_log2 = sm_scale * kLog2e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(g.H * g.nqb), dim3(256), 0, s, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, delta,
@@ -510,7 +557,7 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                      g.kv_rows, g.kv_valid, scale_log2, sm_scale);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(cols), dim3(256), 0, s, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, delta,
-                     col_ptr, row_idx, (uint16_t*)dk, (uint16_t*)dv, g.nqb, g.nkb, g.q_rows,
+                     col_ptr, row_idx, order, (uint16_t*)dk, (uint16_t*)dv, g.nqb, g.nkb, g.q_rows,
                      g.q_valid, g.kv_rows, g.kv_valid, scale_log2, sm_scale);
   return hipGetLastError();
 }

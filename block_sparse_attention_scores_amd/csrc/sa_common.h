@@ -141,7 +141,8 @@ hipError_t launch_backward(const Dims& g, const void* q, const void* k, const vo
                            const void* out, const void* dout, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
                            void* dv, float* delta, uint32_t* bits, int32_t* counts,
-                           int32_t* col_ptr, int32_t* row_idx, float sm_scale, hipStream_t s);
+                           int32_t* col_ptr, int32_t* row_idx, int32_t* order, float sm_scale,
+                           hipStream_t s);
 // Token projections for the token-level estimators: per token the 16 fp64
 // components of x W (128 bytes).
 hipError_t launch_token_projection(const Dims& g, const void* q, const void* k, const float* wq,

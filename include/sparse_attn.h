@@ -319,8 +319,9 @@ int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int
  * dq [H,q_rows,d], dk, dv [H,kv_rows,d]: out, bf16 (fp32 accumulation, P and
  *   dS rounded to bf16 as MFMA operands); padded rows and key blocks that no
  *   query block selected get zero;
- * ws: workspace of sa_workspace_size(SA_STAGE_BACKWARD) bytes (D, and the
- *   transposed block lists: per key block the query blocks that selected it). */
+ * ws: workspace of sa_workspace_size(SA_STAGE_BACKWARD) bytes (D, the
+ *   transposed block lists: per key block the query blocks that selected it,
+ *   and the launch order of the dK/dV work: per head, longest lists first). */
 int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, const void* v,
                          const void* out, const void* dout, const float* lse,
                          const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* dk,
