@@ -429,8 +429,10 @@ def machine_context(flush, reps=5):
     """Context for the roofline fractions, measured on this GPU: compute-unit
     count and architecture (device properties), the engine clock rocminfo
     lists, a 1 GiB device copy (flushed, median of `reps`; read + write bytes
-    over time) and a dense bf16 GEMM through torch.mm (the vendor BLAS,
-    8192 x 8192 x 8192, median of `reps` after one untimed call)."""
+    over time), a dense bf16 GEMM through torch.mm (the vendor BLAS,
+    8192 x 8192 x 8192, median of `reps` after one untimed call) and a
+    register-only MFMA loop (libsa_probe.so), the matrix rate the chip holds
+    with nothing else running."""
     import subprocess
     import torch
     props = torch.cuda.get_device_properties(0)
@@ -462,6 +464,26 @@ def machine_context(flush, reps=5):
     ms = _timed(lambda: torch.mm(a, b, out=c), flush, reps)
     ctx["gemm_bf16_8192_tflops"] = round(2.0 * m ** 3 / (ms / 1e3) / 1e12, 1)
     del a, b, c
+    # matrix pipes alone: 1024 workgroups (four waves per SIMD), each wave 8192
+    # rounds of eight independent v_mfma_f32_32x32x16_bf16 on registers
+    try:
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_scores_amd", "lib",
+                                         "libsa_probe.so"))
+        wgs, iters = 1024, 8192
+        out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def run_probe():
+            if probe.sa_probe_mfma_bf16(wgs, iters, ctypes.c_void_p(out.data_ptr()), stream) != 0:
+                raise RuntimeError("sa_probe_mfma_bf16 failed")
+        run_probe()
+        torch.cuda.synchronize()
+        ms = _timed(run_probe, None, reps)
+        ctx["mfma_bf16_loop_tflops"] = round(wgs * 4 * iters * 8 * 32768 / (ms / 1e3) / 1e12, 1)
+        del out
+    except OSError:
+        ctx["mfma_bf16_loop_tflops"] = None
     torch.cuda.synchronize()
     return ctx
 

@@ -27,6 +27,9 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libsparse_attn.so")
+# measurement context only (bench.py): a matrix-pipe throughput probe
+PROBE_SRC = os.path.join(CSRC, "probe", "mfma_probe.hip")
+PROBE_LIB = os.path.join(LIB_DIR, "libsa_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -111,7 +114,21 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = True) -> str:
+    """libsa_probe.so: the matrix-pipe probe bench.py reports as context."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
