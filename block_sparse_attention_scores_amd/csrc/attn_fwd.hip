@@ -104,6 +104,22 @@ __global__ __launch_bounds__(kQueueThreads) void queue_kernel(const int32_t* __r
   const int heads = rows / qs.nqb;
   const int ng = 2 * (kXcd + ((heads - 1) >> qs.hshift) + 1);
   const int64_t total = row_ptr[rows];
+  if (!split) {
+    // Whole items only: along the item order both the range and the head are
+    // non-decreasing, so the sort is the identity, and range x starts at the
+    // first item whose range is x or more (one pass, no scans).
+    for (int r = t; r < rows; r += kQueueThreads) {
+      units[r] = 2 * r;
+      const int xr = unit_xcd(unit_range(row_ptr, r, 0, 0), total);
+      const int xp = r > 0 ? unit_xcd(unit_range(row_ptr, r - 1, 0, 0), total) : -1;
+      for (int x = xp + 1; x <= xr; ++x) xq[x] = r;
+      if (r == rows - 1)
+        for (int x = xr + 1; x <= kXcd; ++x) xq[x] = rows;
+    }
+    if (t < kXcd) ctr[t] = 0;
+    if (rows == 0 && t <= kXcd) xq[t] = 0;
+    return;
+  }
   for (int b = t; b < ng; b += kQueueThreads) {
     gstart[b] = 0;
     gfirst[b] = INT_MAX;
