@@ -116,7 +116,7 @@ def test_path_in_tile_order(latent, tile, extra):
         f"{O.select(O.scores_for(x['q'], x['k'], w.q_valid, w.kv_valid, w.block, w.score_mode, w.eff_score_scale)[2], w.select_mode, w.top_p, w.top_k)[0].mean():.3f}), excused {exc}")
 
 
-@pytest.mark.parametrize("name", ["480p", "720p_rank"])
+@pytest.mark.parametrize("name", ["480p", "720p_rank", "hetero"])
 def test_full_size_tile_order(name):
     """The benchmark's tile-order leg at full size: selection, CSR and demand
     on every row, attention on sampled items, O and LSE back in raster order;
