@@ -392,7 +392,7 @@ def main():
     if w.dtype == "bf16" and not args.no_extras:
         rec["load_balance"] = load_balance(sa, packed, flush)
         rec["dense_context"] = dense_context(w, d, sa, flush, packed, flops)
-        if w.select_mode == 1 and w.score_mode in (0, 1) and not tiles:
+        if w.score_mode in (0, 1) and not tiles:
             rec["fused"] = fused_leg(w, d, sa, flush, args.steps, ms_step, flops)
         if w.name == "hetero_40h_32k" and not tiles:
             rec["hetero_scale1"] = scale1_leg(w, d, sa, flush, packed)
@@ -563,10 +563,12 @@ def load_balance(sa, packed, flush, reps=5):
 
 def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
     """The fused single pass (sparse_attn_fused: pooling, then one kernel that
-    scores, keeps the top-k and attends per query block) timed like the step:
-    a flush, then the call, ``steps`` times; against the three-call path's ms
-    per layer of the timed steps.  Its kept sets are checked against the
-    three-call path's mask."""
+    scores, selects (top-p with the floor, or top-k) and attends per query
+    block) timed like the step: a flush, then the call, ``steps`` times;
+    against the three-call path's ms per layer of the timed steps.  Its kept
+    sets are compared with the three-call path's mask row by row (in top-p the
+    two sum the masses in different orders, so a row whose cut sits within
+    rounding of p may differ by a block)."""
     import numpy as np
     import torch
     from block_sparse_attention_scores_amd import binding
@@ -585,6 +587,7 @@ def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
     run(bits)
     torch.cuda.synchronize()
     same = bool(torch.equal(bits, sa.mask_bits))
+    rows_differing = int((bits != sa.mask_bits).any(dim=1).sum())
     ts = []
     for r in range(steps):
         _flush(flush, r)
@@ -601,7 +604,8 @@ def fused_leg(w, d, sa, flush, steps, three_call_ms, flops):
             "tflops": round(flops / (ms / 1e3) / 1e12, 3),
             "three_call_ms_per_layer": round(three_call_ms, 4),
             "speedup_over_three_call": round(three_call_ms / ms, 3),
-            "same_mask_as_three_call": same, "steps": steps}
+            "same_mask_as_three_call": same, "rows_differing": rows_differing,
+            "steps": steps}
 
 
 def scale1_leg(w, d, sa, flush, packed, reps=5):

@@ -369,7 +369,7 @@ int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, cons
   Dims g;
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  if (g.dtype != SA_BF16 || g.d != 128 || g.B != 128 || prob->select_mode != SA_TOP_K ||
+  if (g.dtype != SA_BF16 || g.d != 128 || g.B != 128 ||
       (g.score_mode != SA_SCORE_POOLED && g.score_mode != SA_SCORE_LOWRANK))
     return SA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out) return SA_ERR_INVALID_ARG;
@@ -388,12 +388,12 @@ int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, cons
   const float sm = prob->sm_scale > 0.f ? prob->sm_scale : (float)(1.0 / sqrt((double)g.d));
   SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
   if (g.rank > 0) {
-    SA_TRY_HIP(sa::launch_fused_topk(g, qt, kt, g.rank, 1.0, prob->top_k, q, k, v, out, lse_opt,
-                                     mask_bits_opt, sm, s));
+    SA_TRY_HIP(sa::launch_fused(g, qt, kt, g.rank, 1.0, prob->select_mode, (double)prob->top_p,
+                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm, s));
   } else {
     const double sc = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);
-    SA_TRY_HIP(sa::launch_fused_topk(g, qbar, kbar, g.d, sc, prob->top_k, q, k, v, out, lse_opt,
-                                     mask_bits_opt, sm, s));
+    SA_TRY_HIP(sa::launch_fused(g, qbar, kbar, g.d, sc, prob->select_mode, (double)prob->top_p,
+                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm, s));
   }
   return SA_OK;
 }

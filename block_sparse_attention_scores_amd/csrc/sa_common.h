@@ -125,12 +125,13 @@ hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* col_slot, const void* k,
                        const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
                        float sm_scale, int schedule, uint64_t* wg_clock, hipStream_t s);
-// Fused top-k estimation + attention (fused_topk.hip): qx [H*nQB, dim] and
-// kx [H*nKB, dim] fp64 (block means or their projections), S = scale * qx.kx.
-hipError_t launch_fused_topk(const Dims& g, const double* qx, const double* kx, int dim,
-                             double scale, int top_k, const void* q, const void* k, const void* v,
-                             void* out, float* lse, uint32_t* mask_bits, float sm_scale,
-                             hipStream_t s);
+// Fused estimation, selection (mode SA_TOP_P with a top_k floor, or SA_TOP_K)
+// and attention (fused.hip): qx [H*nQB, dim] and kx [H*nKB, dim] fp64 (block
+// means or their projections), S = scale * qx.kx.
+hipError_t launch_fused(const Dims& g, const double* qx, const double* kx, int dim, double scale,
+                        int mode, double top_p, int top_k, const void* q, const void* k,
+                        const void* v, void* out, float* lse, uint32_t* mask_bits, float sm_scale,
+                        hipStream_t s);
 hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int64_t q_start,
                               int64_t q_valid, int32_t* order, int32_t* inverse, int32_t* q_order,
                               int32_t* q_inverse, hipStream_t s);

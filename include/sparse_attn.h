@@ -259,18 +259,25 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q,
 /* Critical-KV estimation and sparse attention in one pass (DSV explainer,
  * "The idea": kernels that fuse the estimation of the critical keys and
  * values with the sparse attention, keep intermediates on chip and never
- * build the full score matrix).  The same result as sparse_attn_select with
- * SA_TOP_K followed by sparse_attn_forward on the full K and V, but after the
- * pooling pass (block means, and their rank-r projections in
- * SA_SCORE_LOWRANK) a single kernel scores each query block against every key
- * block of its head, keeps the min(top_k, nKB) largest scores (ties to the
- * lower block id) and attends to them; no score matrix, mask or CSR goes to
- * memory.
- *   Supported: bf16, head_dim = block = 128, select_mode SA_TOP_K,
- *   score_mode SA_SCORE_POOLED or SA_SCORE_LOWRANK (rank <= 64); else
+ * build the full score matrix).  The same result as sparse_attn_select
+ * followed by sparse_attn_forward on the full K and V, but after the pooling
+ * pass (block means, and their rank-r projections in SA_SCORE_LOWRANK) a
+ * single kernel scores each query block against every key block of its head,
+ * selects as sparse_attn_select does and attends to the kept blocks; no score
+ * matrix, mask or CSR goes to memory.
+ *   SA_TOP_K: the min(top_k, nKB) largest scores (ties to the lower block id).
+ *   SA_TOP_P (Top-p abstract): the shortest prefix of the blocks ranked by
+ *     softmax mass (fp64, ties to the lower id) whose cumulative mass reaches
+ *     top_p, raised to min(top_k, nKB) blocks; top_p >= 1 keeps every block.
+ *     The cumulative mass is summed exactly in 2^-62 fixed point rather than
+ *     as a running fp64 sum.
+ *   Supported: bf16, head_dim = block = 128, nKB <= 4096, score_mode
+ *   SA_SCORE_POOLED or SA_SCORE_LOWRANK (rank <= 64); else
  *   SA_ERR_UNSUPPORTED.  Scores are fp64 (each a sequential fused
  *   multiply-add over the pooled dimension), so the kept sets equal
- *   sparse_attn_select's except where two scores tie to fp64 rounding.
+ *   sparse_attn_select's except where two ranking values tie to fp64
+ *   rounding or, in SA_TOP_P, where top_p lies within rounding of the
+ *   cumulative mass at the cut (one block more or fewer).
  * q [H,q_rows,d], k, v [H,kv_rows,d]: bf16; wq, wk: fp32 [H,d,rank] in
  *   SA_SCORE_LOWRANK (else ignored, may be NULL);
  * out [H,q_rows,d] bf16, lse_opt NULL or fp32 [H,q_rows]: as for

@@ -301,8 +301,9 @@ def test_forward_noalloc_validation(lib):
 
 
 def test_fused_validation(lib):
-    """sparse_attn_fused: only bf16, d = B = 128, fixed top-k over pooled or
-    rank-r scores; argument and workspace errors before any HIP call."""
+    """sparse_attn_fused: only bf16, d = B = 128, top-p (with the floor) or
+    top-k over pooled or rank-r scores; argument and workspace errors before
+    any HIP call."""
     f = lib.sparse_attn_fused
     buf = ctypes.c_void_p(1 << 20)
     ok = good_problem(select_mode=B.SA_TOP_K, top_k=3, score_mode=B.SA_SCORE_LOWRANK, rank=16)
@@ -316,7 +317,12 @@ def test_fused_validation(lib):
     def call(p, q=buf, wq=buf, ws_=ws, n=need):
         return f(ctypes.byref(p), q, buf, buf, wq, buf, buf, None, None, ws_, n, None)
 
-    assert call(good_problem()) == B.SA_ERR_UNSUPPORTED                     # top-p
+    top_p = good_problem(dtype=B.SA_BF16)
+    assert top_p.select_mode == B.SA_TOP_P
+    st_p, need_p = status_of_ws(top_p, B.SA_STAGE_FUSED)
+    assert st_p == 0
+    assert call(top_p, n=need_p - 256) == B.SA_ERR_WORKSPACE             # top-p passes the mode check
+    assert call(good_problem(dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
     assert call(good_problem(select_mode=B.SA_TOP_K, dtype=B.SA_F32)) == B.SA_ERR_UNSUPPORTED
     assert call(good_problem(select_mode=B.SA_TOP_K, head_dim=64)) == B.SA_ERR_UNSUPPORTED
     assert call(good_problem(select_mode=B.SA_TOP_K, score_mode=B.SA_SCORE_LOWRANK_MAX)) == \

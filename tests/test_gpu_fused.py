@@ -1,13 +1,17 @@
-"""GPU parity of the fused single pass (sparse_attn_fused: estimation, top-k
-and attention in one kernel per query block) through the C ABI.
+"""GPU parity of the fused single pass (sparse_attn_fused: estimation,
+selection and attention in one kernel per query block) through the C ABI, in
+both selection modes (top-k, and top-p with a top-k floor).
 
-Bars: the kept sets equal the oracle's top-k on every row except near-ties
-(relative 1e-6 of the row's largest |score|, counted); every row keeps exactly
-min(k, nKB) blocks; attention max-abs error <= 2e-2 against the oracle's dense
-fp32 attention under the fused pass's own mask; and, where the three-call path
-(sparse_attn_select -> sparse_attn_forward on the full K/V) keeps the same
-blocks and does not halve items, the outputs of the two are equal bit for bit
-(the same attention core over the same ascending block lists)."""
+Bars: the kept sets equal the oracle's selection on every row except near-ties
+(relative 1e-6 of the ranking value at the cut, or in top-p a one-block
+difference where p lies within 1e-6 relative of the cumulative mass at the
+cut; counted); top-k rows keep exactly min(k, nKB) blocks and top-p rows at
+least that many; attention max-abs error <= 2e-2 against the oracle's dense
+fp32 attention under the fused pass's own mask; and on every row where the
+three-call path (sparse_attn_select -> sparse_attn_forward on the full K/V)
+keeps the same blocks and does not halve items, the outputs of the two are
+equal bit for bit (the same attention core over the same ascending block
+lists)."""
 import numpy as np
 import pytest
 import torch
@@ -45,26 +49,35 @@ def fused(w, d):
 
 
 def check_fused(w, items=None, compare_three_call=True):
-    say("case", w.name, "heads", w.heads, "nqb", w.n_qb, "nkb", w.n_kb, "k", w.top_k)
+    say("case", w.name, "heads", w.heads, "nqb", w.n_qb, "nkb", w.n_kb, "mode",
+        "top_p" if w.select_mode == I.SELECT_TOP_P else "top_k", "p", w.top_p, "k", w.top_k)
     x = I.generate(w)
     d = to_device(x, w)
     out, lse, bits = fused(w, d)
     mask = O.bits_to_mask(bits.cpu().numpy().view(np.uint32), w.heads, w.n_qb, w.n_kb)
     if w.n_kb % 32:
         assert np.all(bits.cpu().numpy().view(np.uint32)[:, -1] >> np.uint32(w.n_kb % 32) == 0)
-    assert np.all(mask.sum(axis=2) == min(w.top_k, w.n_kb))
+    counts = mask.sum(axis=2)
+    if w.select_mode == I.SELECT_TOP_K:
+        assert np.all(counts == min(w.top_k, w.n_kb))
+    else:
+        assert np.all(counts >= min(w.top_k, w.n_kb)) and np.all(counts >= 1)
     _, _, s = O.scores_for(x["q"], x["k"], w.q_valid, w.kv_valid, w.block, w.score_mode,
                            w.eff_score_scale, x.get("wq"), x.get("wk"))
     excused = 0
     for h in range(w.heads):
         for i in range(w.n_qb):
-            rec = O.select_row_top_k(s[h, i], w.top_k)
+            if w.select_mode == I.SELECT_TOP_K:
+                rec = O.select_row_top_k(s[h, i], w.top_k)
+            else:
+                rec = O.select_row_top_p(s[h, i], w.top_p, w.top_k)
             want = np.zeros(w.n_kb, bool)
             want[rec.order[:rec.m]] = True
             if not np.array_equal(want, mask[h, i]):
-                assert O.row_mismatch_excused(rec, I.SELECT_TOP_K, w.top_p, w.top_k, mask[h, i],
+                assert O.row_mismatch_excused(rec, w.select_mode, w.top_p, w.top_k, mask[h, i],
                                               rel=1e-6), (h, i)
                 excused += 1
+    assert excused <= max(2, w.heads * w.n_qb // 100)
     todo = items if items is not None else [(h, i) for h in range(w.heads) for i in range(w.n_qb)]
     o, l = O.attention(x["q"], x["k"], x["v"], mask, w.q_valid, w.kv_valid, w.block,
                        w.eff_sm_scale, items=todo)
@@ -81,19 +94,26 @@ def check_fused(w, items=None, compare_three_call=True):
     # padded query rows: exactly 0 / -inf, everywhere
     assert np.all(go[:, w.q_valid:] == 0) and np.all(np.isneginf(gl[:, w.q_valid:]))
     assert np.all(np.isfinite(go))
-    same = None
+    rows_same = None
     if compare_three_call:
         sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
         sa.select()
         sa.forward(packed=False)
         torch.cuda.synchronize()
-        same = torch.equal(sa.mask_bits, bits)
-        if same and not items_split(w):
-            assert torch.equal(sa.out, out) and torch.equal(sa.lse, lse)
-        elif same:
-            assert float((sa.out.float() - out.float()).abs().max()) <= TOL_OUT["bf16"]
+        same_row = (sa.mask_bits == bits).all(dim=1).cpu().numpy()
+        rows_same = int(same_row.sum())
+        # the two paths differ only in fp64 summation order: near-cut rows at most
+        assert rows_same >= same_row.size - max(2, same_row.size // 100)
+        # one row per (head, query block) item: q_rows = nQB * B
+        a_o, f_o = sa.out.view(w.heads * w.n_qb, -1), out.view(w.heads * w.n_qb, -1)
+        a_l, f_l = sa.lse.view(w.heads * w.n_qb, -1), lse.view(w.heads * w.n_qb, -1)
+        idx = torch.from_numpy(np.nonzero(same_row)[0]).to("cuda")
+        if not items_split(w):
+            assert torch.equal(a_o[idx], f_o[idx]) and torch.equal(a_l[idx], f_l[idx])
+        else:
+            assert float((a_o[idx].float() - f_o[idx].float()).abs().max()) <= TOL_OUT["bf16"]
     say(f"  excused={excused} attention items={len(todo)} max_abs_err={worst:.3g} "
-        f"same mask as three-call: {same}")
+        f"rows with the three-call path's mask: {rows_same} of {w.heads * w.n_qb}")
     return mask
 
 
@@ -142,6 +162,64 @@ def test_fused_full_size_lowrank():
     against the three-call path bit for bit (same masks, whole items)."""
     w = I.named("lowrank")
     rng = np.random.default_rng(0)
+    rows = w.heads * w.n_qb
+    pick = sorted({0, rows - 1} | set(rng.choice(rows, size=6, replace=False).tolist()))
+    check_fused(w, items=[(r // w.n_qb, r % w.n_qb) for r in pick])
+
+
+def pooled_top_p(**kw):
+    base = dict(name="fused_top_p", heads=2, head_dim=128, block=128, dtype="bf16",
+                latent=(4, 30, 39), q_start=0, q_valid=1000, seed=95, strength=0.5,
+                tile=(2, 4, 4), clusters=6, select_mode=I.SELECT_TOP_P, top_p=0.9, top_k=2,
+                score_mode=I.SCORE_POOLED, score_scale=1.0)
+    base.update(kw)
+    return I.Workload(**base)
+
+
+def test_fused_top_p_pooled_ragged():
+    """Top-p with a floor, pooled scores at temperature 1 (wide kept sets),
+    two mask words, ragged query and key tails."""
+    w = pooled_top_p()
+    assert w.n_kb == 37 and w.kv_valid % w.block and w.q_valid % w.block
+    mask = check_fused(w)
+    assert len(set(mask.sum(axis=2).ravel().tolist())) > 1   # the kept counts vary
+
+
+@pytest.mark.parametrize("p,k", [(1.0, 0), (0.05, 0), (0.05, 9), (0.5, 40)])
+def test_fused_top_p_edges(p, k):
+    """p = 1 keeps every block; a small p keeps the single largest-mass block
+    unless the floor asks for more; a floor at or above nKB keeps every block."""
+    w = pooled_top_p(name=f"fused_top_p_{p}_{k}", top_p=p, top_k=k, seed=96)
+    mask = check_fused(w)
+    counts = mask.sum(axis=2)
+    if p >= 1.0 or k >= w.n_kb:
+        assert mask.all()
+    elif p == 0.05:
+        assert np.all(counts >= max(1, min(k, w.n_kb)))
+
+
+def test_fused_top_p_lowrank():
+    w = lowrank_small(name="fused_top_p_lowrank", select_mode=I.SELECT_TOP_P, top_p=0.9,
+                      top_k=3, seed=97)
+    check_fused(w)
+
+
+def test_fused_top_p_4096_key_blocks():
+    """Top-p over the largest key-block count: 16 keys per thread."""
+    w = pooled_top_p(name="fused_top_p_4096", heads=1, latent=(1, 1, 4096 * 128 - 5), q_valid=300,
+                     tile=(1, 1, 512), clusters=8, strength=1.0, top_p=0.5, top_k=4, seed=98)
+    assert w.n_kb == 4096
+    check_fused(w, items=[(0, 0), (0, 2)], compare_three_call=False)
+
+
+@pytest.mark.parametrize("name", ["480p", "hetero"])
+def test_fused_full_size_top_p(name):
+    """Full-size top-p workloads (the 480p layer at p = 0.9, floor 4; the
+    40-head layer at p = 0.95 with per-head sparsity from about 2% to 60%):
+    every row's kept set against the oracle, attention on sampled items
+    against the oracle, and the three-call path's output, row by row."""
+    w = I.named(name)
+    rng = np.random.default_rng(1)
     rows = w.heads * w.n_qb
     pick = sorted({0, rows - 1} | set(rng.choice(rows, size=6, replace=False).tolist()))
     check_fused(w, items=[(r // w.n_qb, r % w.n_qb) for r in pick])
