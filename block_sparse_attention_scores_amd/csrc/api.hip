@@ -198,7 +198,7 @@ int check_forward_args(const Dims& g, const void* q, const int32_t* row_ptr,
 
 extern "C" {
 
-int sa_abi_version(void) { return 7; }
+int sa_abi_version(void) { return 8; }
 
 const char* sa_status_string(int status) {
   switch (status) {

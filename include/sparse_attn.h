@@ -380,11 +380,12 @@ int sa_permute_rows(int32_t heads, int64_t rows, int32_t row_bytes, const int32_
 /* Static description of a status code (never NULL). */
 const char* sa_status_string(int status);
 
-/* ABI version of this header: 6 (1, plus the video block order entry points
+/* ABI version of this header: 8 (1, plus the video block order entry points
  * in 2, plus sparse_attn_backward in 3, plus sparse_attn_forward_ex and
  * sa_forward_workgroups in 4, plus sparse_attn_forward_noalloc and
  * SA_ERR_SCRATCH in 5, plus sparse_attn_fused and SA_STAGE_FUSED in 6, plus
- * SA_SCHEDULE_AUTO, the per-problem schedule sparse_attn_forward runs, in 7). */
+ * SA_SCHEDULE_AUTO, the per-problem schedule sparse_attn_forward runs, in 7,
+ * plus SA_TOP_P in sparse_attn_fused in 8). */
 int sa_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.sa_abi_version() == 7
+    assert lib.sa_abi_version() == 8
 
 
 def test_struct_layout_matches_c():
