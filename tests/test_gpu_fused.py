@@ -212,10 +212,12 @@ def test_fused_top_p_4096_key_blocks():
     check_fused(w, items=[(0, 0), (0, 2)], compare_three_call=False)
 
 
-@pytest.mark.parametrize("name", ["480p", "hetero"])
+@pytest.mark.parametrize("name", ["480p", "hetero", "720p_rank"])
 def test_fused_full_size_top_p(name):
     """Full-size top-p workloads (the 480p layer at p = 0.9, floor 4; the
-    40-head layer at p = 0.95 with per-head sparsity from about 2% to 60%):
+    40-head layer at p = 0.95 with per-head sparsity from about 2% to 60%;
+    one sequence-parallel rank's 117 query blocks against all 929 key blocks
+    at 720p, p = 0.9, floor 8, four keys per thread in the selection):
     every row's kept set against the oracle, attention on sampled items
     against the oracle, and the three-call path's output, row by row."""
     w = I.named(name)
