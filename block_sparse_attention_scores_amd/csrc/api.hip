@@ -29,6 +29,9 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// 32-bit element arrays (int32 CSR and demand arrays, mask words, fp32
+// weights): NULL counts as aligned, its own check comes first
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Validates the problem and fills the derived sizes.  No HIP call.
 int check_problem(const sa_problem* p, Dims* g) {
@@ -184,13 +187,14 @@ void* scratch_address() {
 
 // Pointer and size checks shared by the forward entry points.
 int check_forward_args(const Dims& g, const void* q, const int32_t* row_ptr,
-                       const int32_t* col_idx, const void* k_src, const void* v_src,
-                       const void* out, const float* lse_opt) {
+                       const int32_t* col_idx, const int32_t* col_slot, const void* k_src,
+                       const void* v_src, const void* out, const float* lse_opt) {
   if (!sa::attn_supported(g.dtype, g.d, g.B)) return SA_ERR_UNSUPPORTED;
   if (!q || !row_ptr || !col_idx || !k_src || !v_src || !out) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(out))
     return SA_ERR_INVALID_ARG;
-  if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
+  if (!aligned4(lse_opt) || !aligned4(row_ptr) || !aligned4(col_idx) || !aligned4(col_slot))
+    return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
 
@@ -234,7 +238,9 @@ int sparse_attn_select(const sa_problem* prob, const void* q, const void* k, con
   if (st != SA_OK) return st;
   if (!q || !k || !mask_bits || !row_ptr || !col_idx) return SA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return SA_ERR_INVALID_ARG;
+  if (!aligned4(mask_bits) || !aligned4(row_ptr) || !aligned4(col_idx)) return SA_ERR_INVALID_ARG;
   if (g.score_mode != SA_SCORE_POOLED && (!wq || !wk)) return SA_ERR_INVALID_ARG;
+  if (g.score_mode != SA_SCORE_POOLED && (!aligned4(wq) || !aligned4(wk))) return SA_ERR_INVALID_ARG;
   if ((qbar_opt && ((uintptr_t)qbar_opt & 7u)) || (kbar_opt && ((uintptr_t)kbar_opt & 7u)))
     return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_SELECT, ws, ws_bytes);
@@ -274,6 +280,7 @@ int sparse_attn_csr_from_mask(const sa_problem* prob, const uint32_t* mask_bits,
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
   if (!mask_bits || !row_ptr || !col_idx) return SA_ERR_INVALID_ARG;
+  if (!aligned4(mask_bits) || !aligned4(row_ptr) || !aligned4(col_idx)) return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_CSR, ws, ws_bytes);
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -296,6 +303,9 @@ int kv_demand_pack(const sa_problem* prob, const int32_t* row_ptr, const int32_t
   if (packed_cap_blocks > 0 && (!k_packed || !v_packed)) return SA_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_packed) || !aligned16(v_packed))
     return SA_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)row_ptr, (const void*)col_idx, (const void*)demand_ptr,
+                        (const void*)demand_idx, (const void*)col_slot, (const void*)dev_status})
+    if (!aligned4(p)) return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_PACK, ws, ws_bytes);
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -334,7 +344,7 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q, const int32_t*
   Dims g;
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  st = check_forward_args(g, q, row_ptr, col_idx, k_src, v_src, out, lse_opt);
+  st = check_forward_args(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt);
   if (st != SA_OK) return st;
   int schedule = resolve_schedule(prob, opts ? opts->schedule : SA_SCHEDULE_AUTO);
   uint64_t* wg_clock = nullptr;
@@ -377,6 +387,7 @@ int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, cons
   if (lse_opt && ((uintptr_t)lse_opt & 3u)) return SA_ERR_INVALID_ARG;
   if (mask_bits_opt && ((uintptr_t)mask_bits_opt & 3u)) return SA_ERR_INVALID_ARG;
   if (g.score_mode == SA_SCORE_LOWRANK && (!wq || !wk)) return SA_ERR_INVALID_ARG;
+  if (g.score_mode == SA_SCORE_LOWRANK && (!aligned4(wq) || !aligned4(wk))) return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_FUSED, ws, ws_bytes);
   if (st != SA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -405,7 +416,7 @@ int sparse_attn_forward_noalloc(const sa_problem* prob, const void* q, const int
   Dims g;
   int st = check_problem(prob, &g);
   if (st != SA_OK) return st;
-  st = check_forward_args(g, q, row_ptr, col_idx, k_src, v_src, out, lse_opt);
+  st = check_forward_args(g, q, row_ptr, col_idx, col_slot, k_src, v_src, out, lse_opt);
   if (st != SA_OK) return st;
   // whole items only: the queue is all the workspace the launch gets
   const size_t need = sa::attn_queue_ws_bytes(g);
@@ -432,6 +443,7 @@ int sparse_attn_backward(const sa_problem* prob, const void* q, const void* k, c
   for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if (!aligned16(p)) return SA_ERR_INVALID_ARG;
   if ((uintptr_t)lse & 15u) return SA_ERR_INVALID_ARG;
+  if (!aligned4(row_ptr) || !aligned4(col_idx)) return SA_ERR_INVALID_ARG;
   st = check_ws(g, SA_STAGE_BACKWARD, ws, ws_bytes);
   if (st != SA_OK) return st;
   const BackwardWs w = backward_ws(g);

@@ -161,6 +161,44 @@ def test_pack_and_forward_argument_errors(lib):
     assert f(*bad) == B.SA_ERR_UNSUPPORTED                     # bf16 attention needs d=B=128
 
 
+def test_int32_arrays_must_be_four_byte_aligned(lib):
+    """Every int32 / uint32 / fp32 array argument is checked for 4-byte
+    alignment on the host, like the 16-byte checks of the bf16 tensors."""
+    p = good_problem()
+    odd = FAKE + 2
+    _, n = status_of_ws(p)
+    sel = [ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, FAKE * 4, n, None]
+    for i in (5, 6, 7):                                        # mask_bits, row_ptr, col_idx
+        bad = list(sel); bad[i] = odd
+        assert lib.sparse_attn_select(*bad) == B.SA_ERR_INVALID_ARG, i
+    lr = good_problem(score_mode=B.SA_SCORE_LOWRANK, rank=16)
+    _, n_lr = status_of_ws(lr)
+    bad = list(sel); bad[0] = ctypes.byref(lr); bad[3] = odd; bad[4] = FAKE; bad[11] = n_lr
+    assert lib.sparse_attn_select(*bad) == B.SA_ERR_INVALID_ARG   # wq
+    _, n = status_of_ws(p, B.SA_STAGE_CSR)
+    for i in (1, 2, 3):
+        args = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE * 4, n, None]
+        args[i] = odd
+        assert lib.sparse_attn_csr_from_mask(*args) == B.SA_ERR_INVALID_ARG, i
+    _, n = status_of_ws(p, B.SA_STAGE_PACK)
+    pack = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE,
+            FAKE * 4, n, None]
+    for i in (1, 2, 5, 6, 7, 11):   # row_ptr, col_idx, demand_ptr, demand_idx, col_slot, status
+        bad = list(pack); bad[i] = odd
+        assert lib.kv_demand_pack(*bad) == B.SA_ERR_INVALID_ARG, i
+    _, n = status_of_ws(p, B.SA_STAGE_FORWARD)
+    fwd = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE * 4, n, None]
+    for i in (2, 3, 4):                                        # row_ptr, col_idx, col_slot
+        bad = list(fwd); bad[i] = odd
+        assert lib.sparse_attn_forward(*bad) == B.SA_ERR_INVALID_ARG, i
+    _, n = status_of_ws(p, B.SA_STAGE_BACKWARD)
+    bwd = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+           FAKE * 4, n, None]
+    for i in (7, 8):                                           # row_ptr, col_idx
+        bad = list(bwd); bad[i] = odd
+        assert lib.sparse_attn_backward(*bad) == B.SA_ERR_INVALID_ARG, i
+
+
 def test_csr_argument_errors(lib):
     p = good_problem()
     _, n = status_of_ws(p, B.SA_STAGE_CSR)
