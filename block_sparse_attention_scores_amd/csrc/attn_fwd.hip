@@ -337,29 +337,40 @@ __device__ __forceinline__ void attend_item(
     int merge = *flag;
     __syncthreads();
     if (!merge) {
-      // the other half has not published: publish this one (stores, release
-      // fence, then the count); whichever half counts second combines
+      // the other half has not published: publish this one, then count;
+      // whichever half counts second combines.  The partial state goes out
+      // as device-coherent stores (they write through the XCD's L2) and each
+      // lane waits for its own to complete before the barrier, so no
+      // device-scope fence (a write-back and invalidate of the whole L2,
+      // which would drop the key/value blocks the XCD's other workgroups
+      // are reading) is needed.
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          reinterpret_cast<float4*>(mine)[(4 * u + r4) * 256 + tid] =
-              make_float4(st.oacc[u][4 * r4], st.oacc[u][4 * r4 + 1], st.oacc[u][4 * r4 + 2],
-                          st.oacc[u][4 * r4 + 3]);
-      mine[kPartO + tid] = st.m_run;
-      mine[kPartO + 256 + tid] = st.l_run;
-      __threadfence();
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            __hip_atomic_store(&mine[((4 * u + r4) * 256 + tid) * 4 + x], st.oacc[u][4 * r4 + x],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&mine[kPartO + tid], st.m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&mine[kPartO + 256 + tid], st.l_run, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // this lane's stores have completed
       __syncthreads();
-      if (tid == 0) *flag = atomicAdd(&done[item], 1);
+      if (tid == 0)
+        *flag = __hip_atomic_fetch_add(&done[item], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       merge = *flag;
       if (!merge) return;
     }
-    __threadfence();   // acquire: the other half's stores precede its count
+    // The other half's state was complete before its count, which this half
+    // has seen; device-coherent loads read it past any stale L2 copy.
     // Combine in fixed half order (half 0 first), so the result does not
     // depend on which half finished first: with M = max(m0, m1),
     //   O = O1 * 2^(m1 - M) + O0 * 2^(m0 - M),  l likewise.
-    const float m_o = other[kPartO + tid], l_o = other[kPartO + 256 + tid];
+    const float m_o = __hip_atomic_load(&other[kPartO + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float l_o =
+        __hip_atomic_load(&other[kPartO + 256 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float m0 = part ? m_o : st.m_run, m1 = part ? st.m_run : m_o;
     const float l0 = part ? l_o : st.l_run, l1 = part ? st.l_run : l_o;
     const float mm = fmaxf(m0, m1);
@@ -370,8 +381,11 @@ __device__ __forceinline__ void attend_item(
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 ot = reinterpret_cast<const float4*>(other)[(4 * u + r4) * 256 + tid];
-        const float ov[4] = {ot.x, ot.y, ot.z, ot.w};
+        float ov[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          ov[x] = __hip_atomic_load(&other[((4 * u + r4) * 256 + tid) * 4 + x], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const float own = st.oacc[u][4 * r4 + x];
