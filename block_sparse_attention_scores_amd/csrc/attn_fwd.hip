@@ -328,8 +328,10 @@ __device__ __forceinline__ void attend_item(
                 q_rows, kv_valid, scale_log2);
 
   if (range.halved) {
-    // Partial state of this half, lane-major so that each store instruction
-    // covers 1 KiB: O chunk c = 4u + r4 of lane tid at float4 c*256 + tid.
+    // Partial state of this half: value x of O chunk c = 4u + r4 of lane tid
+    // at float (4c + x)*256 + tid, so that each single-word store or load
+    // instruction of a wave covers 256 contiguous bytes (whole lines, which
+    // matters for stores that write through the L2).
     float* mine = partial + ((size_t)item * 2 + part) * kSlotFloats;
     const float* other = partial + ((size_t)item * 2 + (part ^ 1)) * kSlotFloats;
     if (tid == 0) *flag = __hip_atomic_load(&done[item], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -350,7 +352,7 @@ __device__ __forceinline__ void attend_item(
         for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            __hip_atomic_store(&mine[((4 * u + r4) * 256 + tid) * 4 + x], st.oacc[u][4 * r4 + x],
+            __hip_atomic_store(&mine[(4 * (4 * u + r4) + x) * 256 + tid], st.oacc[u][4 * r4 + x],
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&mine[kPartO + tid], st.m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&mine[kPartO + 256 + tid], st.l_run, __ATOMIC_RELAXED,
@@ -384,7 +386,7 @@ __device__ __forceinline__ void attend_item(
         float ov[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          ov[x] = __hip_atomic_load(&other[((4 * u + r4) * 256 + tid) * 4 + x], __ATOMIC_RELAXED,
+          ov[x] = __hip_atomic_load(&other[(4 * (4 * u + r4) + x) * 256 + tid], __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
