@@ -133,9 +133,10 @@ BackwardWs backward_ws(const Dims& g) {
 
 // The fused pass needs the select stage's block means and projections only:
 // the head of the select layout, up to the end of the key projections.
-size_t fused_ws(const Dims& g) {
+size_t fused_ctr(const Dims& g) {
   return select_ws(g).kt + round_up(sizeof(double) * g.H * g.nkb * g.rank);
 }
+size_t fused_ws(const Dims& g) { return fused_ctr(g) + round_up(sizeof(int32_t) * 8); }
 
 size_t stage_bytes(const Dims& g, int stage) {
   switch (stage) {
@@ -400,11 +401,13 @@ int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, cons
   SA_TRY_HIP(sa::launch_pool(g, q, k, wq, wk, qbar, kbar, qt, kt, s));
   if (g.rank > 0) {
     SA_TRY_HIP(sa::launch_fused(g, qt, kt, g.rank, 1.0, prob->select_mode, (double)prob->top_p,
-                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm, s));
+                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm,
+                                at<int32_t>(ws, fused_ctr(g)), s));
   } else {
     const double sc = prob->score_scale > 0.f ? (double)prob->score_scale : 1.0 / sqrt((double)g.d);
     SA_TRY_HIP(sa::launch_fused(g, qbar, kbar, g.d, sc, prob->select_mode, (double)prob->top_p,
-                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm, s));
+                                prob->top_k, q, k, v, out, lse_opt, mask_bits_opt, sm,
+                                at<int32_t>(ws, fused_ctr(g)), s));
   }
   return SA_OK;
 }

@@ -131,7 +131,7 @@ hipError_t launch_attn(const Dims& g, const void* q, const int32_t* row_ptr,
 hipError_t launch_fused(const Dims& g, const double* qx, const double* kx, int dim, double scale,
                         int mode, double top_p, int top_k, const void* q, const void* k,
                         const void* v, void* out, float* lse, uint32_t* mask_bits, float sm_scale,
-                        hipStream_t s);
+                        int32_t* ctr, hipStream_t s);
 hipError_t launch_video_order(int T, int Hl, int Wl, int tt, int th, int tw, int64_t q_start,
                               int64_t q_valid, int32_t* order, int32_t* inverse, int32_t* q_order,
                               int32_t* q_inverse, hipStream_t s);
