@@ -285,7 +285,8 @@ int sparse_attn_forward_ex(const sa_problem* prob, const void* q,
  * mask_bits_opt: NULL, or out uint32 [H*nQB, W] (the kept sets, laid out as
  *   sparse_attn_select writes them), for checking;
  * ws: workspace of sa_workspace_size(SA_STAGE_FUSED) bytes (the block means
- *   and projections). */
+ *   and projections, and in SA_TOP_P the counters of the per-XCD item
+ *   queues, which the call zeroes itself). */
 int sparse_attn_fused(const sa_problem* prob, const void* q, const void* k, const void* v,
                       const float* wq, const float* wk, void* out, float* lse_opt,
                       uint32_t* mask_bits_opt, void* ws, size_t ws_bytes, void* stream);
