@@ -175,6 +175,12 @@ def test_int32_arrays_must_be_four_byte_aligned(lib):
     _, n_lr = status_of_ws(lr)
     bad = list(sel); bad[0] = ctypes.byref(lr); bad[3] = odd; bad[4] = FAKE; bad[11] = n_lr
     assert lib.sparse_attn_select(*bad) == B.SA_ERR_INVALID_ARG   # wq
+    ok = good_problem(select_mode=B.SA_TOP_K, top_k=3, score_mode=B.SA_SCORE_LOWRANK, rank=16)
+    _, n_f = status_of_ws(ok, B.SA_STAGE_FUSED)
+    fz = [ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE * 4, n_f, None]
+    for i in (4, 5):                                           # wq, wk
+        bad = list(fz); bad[i] = odd
+        assert lib.sparse_attn_fused(*bad) == B.SA_ERR_INVALID_ARG, i
     _, n = status_of_ws(p, B.SA_STAGE_CSR)
     for i in (1, 2, 3):
         args = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE * 4, n, None]

@@ -225,3 +225,23 @@ def test_fused_full_size_top_p(name):
     rows = w.heads * w.n_qb
     pick = sorted({0, rows - 1} | set(rng.choice(rows, size=6, replace=False).tolist()))
     check_fused(w, items=[(r // w.n_qb, r % w.n_qb) for r in pick])
+
+
+@pytest.mark.parametrize("mode", ["top_k", "top_p"])
+def test_fused_optional_outputs(mode):
+    """Without the optional LSE and mask-word outputs (NULL) the output is the
+    same, bit for bit, as with them."""
+    w = (lowrank_small(name="fused_opt_k") if mode == "top_k" else
+         pooled_top_p(name="fused_opt_p"))
+    x = I.generate(w)
+    d = to_device(x, w)
+    out, lse, bits = fused(w, d)
+    prob = problem_for(w)
+    n = B.sa_workspace_size(prob, B.SA_STAGE_FUSED)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    out2 = torch.full_like(out, float("nan"))
+    lowrank = w.score_mode == I.SCORE_LOWRANK
+    B.sparse_attn_fused(prob, d["q"], d["k"], d["v"], d["wq"] if lowrank else None,
+                        d["wk"] if lowrank else None, out2, None, None, ws, n)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
