@@ -159,23 +159,31 @@ def test_backward_deterministic_and_empty_rows():
     assert np.all(got[1][1, 2 * w.block:3 * w.block] == 0)
 
 
-def test_backward_full_size_sampled():
-    """480p at full size, after the GPU's own select and forward.  Checked: dQ
-    of sampled query blocks, and dK, dV of one key block over every query
-    block that selected it.  For those query blocks the backward gets the
-    oracle's O and LSE (the other rows keep the GPU forward's), so each
+@pytest.mark.parametrize("name", ["480p", "hetero", "lowrank"])
+def test_backward_full_size_sampled(name):
+    """Full size, after the GPU's own select and forward (480p; the 40-head
+    layer, on its sparsest head; the low-rank workload, 1024 key blocks of
+    which each query block keeps 102).  Checked: dQ of sampled query blocks,
+    and dK, dV of one key block over every query block that selected it (at
+    480p the middle one, elsewhere the one with the longest list, which the
+    dK/dV launch order starts with).  For those query blocks the backward gets
+    the oracle's O and LSE (the other rows keep the GPU forward's), so each
     checked gradient depends on oracle-provided forward outputs only."""
     from test_gpu_fullsize import sampled_items
-    w = I.named("480p")
+    w = I.named(name)
     say("backward full size", w.name)
     x = I.generate(w)
     d = to_device(x, w)
-    sa = SparseAttention(w, d["q"], d["k"], d["v"])
+    sa = SparseAttention(w, d["q"], d["k"], d["v"], d.get("wq"), d.get("wk"))
     sa.run(packed=True)
     torch.cuda.synchronize()
     mask = O.bits_to_mask(sa.mask_bits.cpu().numpy().view(np.uint32), w.heads, w.n_qb, w.n_kb)
     rp, _ = sa.host_csr()
-    h0, j0 = 5, w.n_kb // 2
+    if name == "480p":
+        h0, j0 = 5, w.n_kb // 2
+    else:
+        h0 = int(np.argmin(mask.sum(axis=(1, 2)))) if name == "hetero" else w.heads // 2
+        j0 = int(np.argmax(mask[h0].sum(axis=0)))
     col_items = [(h0, i) for i in range(w.n_qb) if mask[h0, i, j0]]
     items = sorted(set(col_items) | set(sampled_items(w, rp, n_random=3)))
     say(f"  {len(col_items)} query blocks select key block ({h0}, {j0}); {len(items)} items")
